@@ -1,0 +1,186 @@
+"""CPU oracle for exact scaled-dot-product attention (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's
+CPU-baseline leg use it. It shares no code with the HIP library; its inputs
+are plain float64 arrays decoded from the seeded generator.
+
+What it computes, and where that is defined:
+
+* ``attention`` is the plain definition written out: scores S = scale * Q K^T,
+  the causal mask, a max-subtracted row softmax P, then O = P V, one (b, h)
+  head at a time, with S and P fully materialised. This is the three-step
+  naive attention of "Describe Flash Attention at a high level"
+  (mantramindai.in), section "What naive attention does", and of "How
+  FlashAttention Speeds Up the Attention Layer" (hassanahmed.net), the
+  section on the obvious three-step formulation. The max subtraction is the
+  numerical-stability step the hassanahmed.net page describes in its online
+  softmax section. It also returns the per-row log-sum-exp
+  LSE_i = ln sum_j exp(S_ij), which the pages do not define (reading: natural
+  log over the visible keys, in float).
+* ``online_attention`` follows the streaming recurrence of the mantramindai.in
+  page, section "The two ideas", idea 2 and its numpy listing: keep a running
+  max m, running sum l and running output per query row; for each key block,
+  raise m to the block max, shrink the old l and output by exp(m_old - m_new),
+  add the block, and divide by l once at the end. It is an oracle of the
+  algorithm the fused kernel runs, pinned against ``attention``.
+* ``split_decode`` follows the same page's follow-up on decode (Flash-Decoding):
+  one query row, the keys cut into chunks that are processed independently,
+  each chunk yielding (max, sum, unnormalised output), and the chunks merged
+  with the same max-and-sum rule.
+* ``decode`` is the plain definition for one query row per head.
+
+Readings where the pages are silent (also listed in the design notes):
+  - scale is a caller argument; the pages write 1/sqrt(d); the oracle rounds
+    it to float32 first, as the kernels receive a float32;
+  - causal: key j is visible to query i iff j <= i (same N for Q and K);
+  - masked logits are -inf before the row max; every row sees key 0.
+
+Pins: every function here is pinned by tests/test_oracle.py against brute
+force, closed forms and invariants (see that file); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f32(scale: float) -> float:
+    """The float32 value the kernels receive for ``scale``, as float64."""
+    return float(np.float32(scale))
+
+
+def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, s: float, rows=None):
+    """Naive attention for one head. q: [N,d], k/v: [Nk,d]; rows: optional query-row subset."""
+    qi = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    S = s * (q[qi] @ k.T)                                  # scores, [len(qi), Nk]
+    if causal:
+        S = np.where(np.arange(k.shape[0])[None, :] > qi[:, None], -np.inf, S)
+    m = S.max(axis=1, keepdims=True)                       # row max (finite: key 0 is visible)
+    P = np.exp(S - m)                                      # exp(-inf) = 0 for masked keys
+    l = P.sum(axis=1, keepdims=True)
+    P = P / l                                              # softmax
+    O = P @ v
+    lse = m[:, 0] + np.log(l[:, 0])
+    return O, lse, P
+
+
+def attention(q, k, v, causal: bool, scale: float, rows=None, heads=None):
+    """Exact attention by the plain definition.
+
+    q, k, v: float64 arrays [B, H, N, d] (k, v may have Nk rows). Returns
+    (O [B,H,len(rows),d], LSE [B,H,len(rows)]), computed one head at a time.
+    ``rows`` restricts the query rows (for sampled checks at large N);
+    ``heads`` restricts the (b, h) pairs (others are left as NaN).
+    """
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    B, H, N, d = q.shape
+    nr = N if rows is None else len(rows)
+    O = np.full((B, H, nr, v.shape[-1]), np.nan)
+    L = np.full((B, H, nr), np.nan)
+    s = _f32(scale)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        O[b, h], L[b, h], _ = _head_attention(q[b, h], k[b, h], v[b, h], causal, s, rows)
+    return O, L
+
+
+def attention_probs(q, k, causal: bool, scale: float):
+    """The materialised probability matrix P for one head (q, k: [N,d])."""
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    return _head_attention(q, k, np.zeros((k.shape[0], 1)), causal, _f32(scale))[2]
+
+
+def online_attention(q, k, v, causal: bool, scale: float, block: int):
+    """The streaming (online-softmax) recurrence over key blocks, float64, one head.
+
+    q: [N,d], k/v: [Nk,d]. Returns (O, LSE). For every query row: running
+    max m (starts at -inf), running sum l (0) and running output acc (0);
+    per key block: m_new = max(m, block max); shrink l and acc by
+    exp(m - m_new); add exp(scores - m_new) to l and its V-weighted sum to
+    acc; at the end O = acc / l and LSE = m + ln l.
+    """
+    q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
+    s = _f32(scale)
+    N, Nk = q.shape[0], k.shape[0]
+    O = np.zeros((N, v.shape[1]))
+    L = np.zeros(N)
+    for i in range(N):
+        m, l, acc = -np.inf, 0.0, np.zeros(v.shape[1])
+        for start in range(0, Nk, block):
+            stop = min(Nk, start + block)
+            if causal:
+                stop = min(stop, i + 1)                   # keys beyond i are masked
+            if stop <= start:
+                break
+            sb = s * (k[start:stop] @ q[i])
+            m_new = max(m, sb.max())
+            shrink = np.exp(m - m_new)                     # exp(-inf) = 0 on the first block
+            pb = np.exp(sb - m_new)
+            l = l * shrink + pb.sum()
+            acc = acc * shrink + pb @ v[start:stop]
+            m = m_new
+        O[i] = acc / l
+        L[i] = m + np.log(l)
+    return O, L
+
+
+def decode(q, kc, vc, scale: float | None = None):
+    """One query row per head over a whole cache, by the plain definition.
+
+    q: [B,H,d] (or [B,H,1,d]); kc, vc: [B,H,Lkv,d]. Non-causal over the
+    cache. scale defaults to 1/sqrt(d) (rounded to float32). Returns
+    (o [B,H,d], lse [B,H]).
+    """
+    q = np.asarray(q, np.float64)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    kc, vc = np.asarray(kc, np.float64), np.asarray(vc, np.float64)
+    d = q.shape[-1]
+    s = _f32(1.0 / np.sqrt(d) if scale is None else scale)
+    B, H = q.shape[:2]
+    o = np.empty((B, H, vc.shape[-1]))
+    lse = np.empty((B, H))
+    for b in range(B):
+        for h in range(H):
+            O, L, _ = _head_attention(q[b, h][None, :], kc[b, h], vc[b, h], False, s)
+            o[b, h], lse[b, h] = O[0], L[0]
+    return o, lse
+
+
+def split_decode(q, kc, vc, nsplit: int, scale: float | None = None):
+    """Flash-Decoding for one head: split the keys, reduce each chunk, merge.
+
+    q: [d]; kc, vc: [Lkv, d]. The keys are cut into chunks of
+    ceil(Lkv / nsplit) rows (the last chunk shorter; nsplit is first clamped
+    to Lkv). Each chunk yields its max m_s, its sum l_s = sum exp(score - m_s)
+    and its unnormalised output o_s = sum exp(score - m_s) v. The merge takes
+    M = max m_s, weights w_s = exp(m_s - M), L = sum w_s l_s and
+    o = sum w_s o_s / L. Returns (o, lse).
+    """
+    q, kc, vc = (np.asarray(t, np.float64) for t in (q, kc, vc))
+    Lkv, d = kc.shape
+    s = _f32(1.0 / np.sqrt(d) if scale is None else scale)
+    nsplit = max(1, min(nsplit, Lkv))
+    chunk = -(-Lkv // nsplit)
+    parts = []
+    for start in range(0, Lkv, chunk):
+        sc = s * (kc[start:start + chunk] @ q)
+        m_s = sc.max()
+        p = np.exp(sc - m_s)
+        parts.append((m_s, p.sum(), p @ vc[start:start + chunk]))
+    M = max(p[0] for p in parts)
+    w = [np.exp(m_s - M) for m_s, _, _ in parts]
+    L = sum(wi * l_s for wi, (_, l_s, _) in zip(w, parts))
+    o = sum(wi * o_s for wi, (_, _, o_s) in zip(w, parts)) / L
+    return o, M + np.log(L)
+
+
+def naive_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
+    """Bytes of one materialised N x N score (or probability) matrix for all heads."""
+    return B * H * N * N * elem_bytes
+
+
+def attention_flops(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Algorithmic forward FLOPs: 4*d per visible (query, key) pair (QK^T and PV)."""
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4 * d * B * H * pairs

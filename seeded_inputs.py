@@ -1,0 +1,154 @@
+"""Seeded synthetic inputs shared by the oracle side and the HIP side.
+
+This module holds random draws and the fp32 -> bf16 input cast only; it holds
+none of the attention arithmetic. Both the CPU oracle's tests and the GPU
+tests/bench draw their Q, K, V here, so the two sides see identical values.
+
+Recipe (same for every workload):
+  * one numpy PCG64 stream per (workload id, tensor, batch index, head index),
+    seeded with the sequence [0, workload id, tensor id, b, h], so any single
+    head can be regenerated alone;
+  * values i.i.d. standard normal drawn in float32;
+  * an optional exact multiplier (the 8K workload doubles K, which is exact in
+    bf16 because it only moves the exponent);
+  * for bf16 workloads, round-to-nearest-even to bf16. The bf16 bit patterns
+    are what the GPU receives and what the oracle decodes to float64.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+
+import numpy as np
+
+BASE_SEED = 0
+TENSOR_ID = {"q": 0, "k": 1, "v": 2}
+
+
+@dataclass(frozen=True)
+class Workload:
+    wid: int            # workload id, part of every seed
+    name: str
+    B: int
+    H: int
+    N: int              # query rows per head (1 for decode)
+    d: int
+    dtype: str          # "f32" or "bf16"
+    causal: bool
+    decode: bool = False
+    Lkv: int = 0        # decode cache length
+    nsplit: int = 0     # decode split count
+    k_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d), rounded to float32 (the value the kernels receive)."""
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    @property
+    def nk(self) -> int:
+        """Number of key rows per head."""
+        return self.Lkv if self.decode else self.N
+
+
+# The five workloads of this library's test and benchmark plan.
+WORKLOADS = {
+    "f32_n256_d64": Workload(1, "f32_n256_d64", 1, 1, 256, 64, "f32", False),
+    "bf16_b4h16_n1024_d64_causal": Workload(2, "bf16_b4h16_n1024_d64_causal", 4, 16, 1024, 64, "bf16", True),
+    "bf16_h32_n8192_d128_causal_k2": Workload(3, "bf16_h32_n8192_d128_causal_k2", 1, 32, 8192, 128, "bf16", True,
+                                              k_mult=2.0),
+    "bf16_h32_n16384_d128_causal": Workload(4, "bf16_h32_n16384_d128_causal", 1, 32, 16384, 128, "bf16", True),
+    "decode_b16h32_l32768_d128": Workload(5, "decode_b16h32_l32768_d128", 16, 32, 1, 128, "bf16", False,
+                                          decode=True, Lkv=32768, nsplit=64),
+}
+
+
+def normal_f32(wid: int, tensor: str, b: int, h: int, shape) -> np.ndarray:
+    """i.i.d. N(0,1) float32 draws for one (workload, tensor, b, h) slice."""
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, wid, TENSOR_ID[tensor], b, h]))
+    return rng.standard_normal(shape, dtype=np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 with round-to-nearest-even; returns uint16 bit patterns.
+
+    Inputs here are finite normal draws, so NaN handling is not needed; a NaN
+    input is rejected rather than silently rounded.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("f32_to_bf16_bits expects finite inputs")
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _slice_values(w: Workload, tensor: str, b: int, h: int, rows: int) -> np.ndarray:
+    x = normal_f32(w.wid, tensor, b, h, (rows, w.d))
+    if tensor == "k" and w.k_mult != 1.0:
+        x = (x * np.float32(w.k_mult)).astype(np.float32)
+    return x
+
+
+def tensor_slice(w: Workload, tensor: str, b: int, h: int) -> np.ndarray:
+    """One head of one tensor, as the kernels receive it.
+
+    Returns uint16 bf16 bit patterns for bf16 workloads, float32 otherwise.
+    Shape [rows, d], rows = N for q (1 for decode) and nk for k/v.
+    """
+    rows = (1 if w.decode else w.N) if tensor == "q" else w.nk
+    x = _slice_values(w, tensor, b, h, rows)
+    return f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+
+
+def tensor_full(w: Workload, tensor: str, heads=None, threads: int | None = None) -> np.ndarray:
+    """Whole [B, H, rows, d] tensor (or only the (b, h) pairs in ``heads``, others zero).
+
+    Slices are generated in parallel threads; numpy releases the GIL while it
+    fills them.
+    """
+    rows = (1 if w.decode else w.N) if tensor == "q" else w.nk
+    dt = np.uint16 if w.dtype == "bf16" else np.float32
+    out = np.zeros((w.B, w.H, rows, w.d), dtype=dt)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)] if heads is None else list(heads)
+
+    def fill(bh):
+        b, h = bh
+        out[b, h] = tensor_slice(w, tensor, b, h)
+
+    nthreads = threads or min(16, len(os.sched_getaffinity(0)))
+    if len(pairs) <= 1 or nthreads <= 1:
+        for bh in pairs:
+            fill(bh)
+    else:
+        with ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(fill, pairs))
+    return out
+
+
+def as_float64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode kernel-input values (bf16 bits or float32) to float64, exactly."""
+    if dtype == "bf16":
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def random_case(seed: int, B: int, H: int, N: int, d: int, dtype: str, nk: int | None = None, std: float = 1.0):
+    """Small ad-hoc case for ragged-shape tests: returns (q, k, v) kernel inputs.
+
+    q is [B,H,N,d]; k, v are [B,H,nk,d] (nk defaults to N). Values are
+    std * N(0,1), cast to bf16 (RNE) for bf16 cases.
+    """
+    nk = N if nk is None else nk
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 1000 + seed, B, H, N, d, nk]))
+    outs = []
+    for rows in (N, nk, nk):
+        x = (rng.standard_normal((B, H, rows, d), dtype=np.float32) * np.float32(std)).astype(np.float32)
+        outs.append(f32_to_bf16_bits(x) if dtype == "bf16" else x)
+    return tuple(outs)
