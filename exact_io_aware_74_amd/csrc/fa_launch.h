@@ -1,0 +1,24 @@
+// Host-side launchers of the attention kernels (internal to the library; the
+// public surface is the C ABI in fa.h). Arguments are assumed validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, bool causal, float scale, hipStream_t s);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int B, int H, int N, int d, bool causal, float scale, hipStream_t s);
+
+// Decode: `chunk` keys per split, `nsplit` splits (every split non-empty).
+// `ws` holds B*H*nsplit*(d+2) floats.
+hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* ws,
+                         int B, int H, int Lkv, int d, int nsplit, int chunk, hipStream_t s);
+
+// Naive three-kernel ablation; `S` holds B*H*N*N floats.
+hipError_t launch_naive(const void* q, const void* k, const void* v, void* o, float* lse, float* S,
+                        int B, int H, int N, int d, bool causal, float scale, hipStream_t s);
+
+}  // namespace fa

@@ -1,0 +1,142 @@
+/*
+ * fa.h -- C ABI of an MI355X (gfx950) library for exact scaled-dot-product
+ * attention: a fused, tiled forward pass with online softmax (prefill), a
+ * split-KV decode with a max-and-sum merge, and a deliberately naive
+ * three-kernel path kept for comparison.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major and contiguous. Q, K, V and O are [B, H, N, d]
+ *   with d contiguous; LSE is [B, H, N] float32. Decode Q and O are [B, H, d],
+ *   the caches [B, H, Lkv, d].
+ * - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *   never frees them and never keeps them past the call. Every tensor pointer
+ *   must be 16-byte aligned.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream) on the current
+ *   device. Calls only enqueue work and return; results are ready once the
+ *   caller synchronises with that stream. Errors raised while the kernels run
+ *   surface at that synchronisation, not in the return value.
+ * - Arguments are fully validated before anything is enqueued: a call that
+ *   returns an error has had no device side effects.
+ * - Sizes are int; every element offset is computed in 64-bit.
+ * - A size of zero (B, H or N equal to 0) is an empty problem: the call returns
+ *   FA_OK and enqueues nothing (pointers may then be NULL).
+ * - Return value: FA_OK (0) or a negative FA_ERR_* code; fa_status_str()
+ *   names it. After FA_ERR_HIP, fa_last_hip_error() returns the hipError_t.
+ *
+ * The method is described on "Describe Flash Attention at a high level"
+ * (mantramindai.in) and "How FlashAttention Speeds Up the Attention Layer"
+ * (hassanahmed.net). The pages give no programming interface; they only say
+ * the kernel is normally reached through a framework.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, negative size, bad scale or nsplit */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension d other than 64 or 128 */
+  FA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  FA_ERR_NOMEM = -4        /* the library could not allocate its decode workspace */
+};
+
+/*
+ * fa_fwd -- fused exact attention forward, bf16 inputs and output.
+ *
+ * O = softmax(scale * Q K^T [+ causal mask]) V, computed per query tile in one
+ * pass over the key tiles with the online-softmax recurrence (running row max,
+ * running sum, output rescaled by exp(m_old - m_new) when the max rises), so
+ * the N x N score matrix is never written to memory. Sources: mantramindai.in,
+ * section "The two ideas" (tiling, online softmax); hassanahmed.net, the
+ * sections on tiling and on the online softmax.
+ *
+ *   q, k, v  const bf16 [B,H,N,d]; o: bf16 [B,H,N,d] (may not alias q, k, v)
+ *   lse      float32 [B,H,N], natural-log log-sum-exp of each row's scaled
+ *            logits over its visible keys; NULL = not written
+ *   causal   nonzero: key j is visible to query i iff j <= i
+ *   scale    multiplier of the logits; must be finite and >= 0
+ *   d        64 or 128 (else FA_ERR_UNSUPPORTED)
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; softmax in fp32; the
+ * probabilities are rounded to bf16 (round to nearest even) for the P V
+ * product; O is divided by the row sum in fp32 and rounded once to bf16.
+ * Uses no workspace and allocates nothing.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_f32 -- the same operation as fa_fwd with float32 Q, K, V and O, and
+ * float32 arithmetic throughout (no bf16 rounding anywhere). Same arguments,
+ * layouts and errors as fa_fwd.
+ */
+int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_decode -- attention of one new query row per (b, h) over a whole KV cache,
+ * split across workgroups (Flash-Decoding): the cache is cut into nsplit chunks
+ * of ceil(Lkv/nsplit) keys; each chunk yields its max, its sum of exponentials
+ * and its unnormalised output; a second kernel merges the chunks with the same
+ * max-and-sum rule as the online softmax. Source: mantramindai.in, section
+ * "Follow-up questions to expect", the question on decode.
+ *
+ *   q               const bf16 [B,H,d]
+ *   kcache, vcache  const bf16 [B,H,Lkv,d]
+ *   o               bf16 [B,H,d]
+ *   Lkv             >= 1 (no mask: every cached key is visible)
+ *   nsplit          >= 1; clamped so that no chunk is empty
+ *   d               64 or 128
+ * The logit scale is 1/sqrt(d) (rounded to float32).
+ * Workspace: the library owns one float32 partials buffer per (device, stream),
+ * grown on demand (hipMalloc) and freed by fa_shutdown(); growing it first
+ * synchronises `stream`. Calls on one stream are ordered; calls on different
+ * streams use different buffers. FA_ERR_NOMEM if the buffer cannot be grown.
+ */
+int fa_decode(const void* q, const void* kcache, const void* vcache, void* o,
+              int B, int H, int Lkv, int d, int nsplit, void* stream);
+
+/* Bytes of decode partials for this shape (the buffer fa_decode keeps). */
+size_t fa_decode_workspace_bytes(int B, int H, int Lkv, int d, int nsplit);
+
+/*
+ * fa_naive_fwd -- the three-step attention of the pages, kept as an ablation:
+ * kernel 1 writes S = scale * Q K^T (masked entries -inf) to `workspace` as
+ * float32 [B,H,N,N]; kernel 2 turns each row into softmax probabilities in
+ * place and writes LSE; kernel 3 reads P back and writes O = P V. The N x N
+ * matrix makes every step an HBM round trip. Sources: mantramindai.in,
+ * section "What naive attention does"; hassanahmed.net, the three-step
+ * formulation.
+ *
+ * Same q, k, v, o, lse, B, H, N, d, causal, scale as fa_fwd (bf16 inputs and
+ * output; S, P and the products in float32). `workspace` is a caller-owned
+ * device buffer of at least fa_naive_workspace_bytes(B,H,N) bytes, passed in
+ * `workspace_bytes` (too small: FA_ERR_INVALID_ARG).
+ */
+int fa_naive_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, int causal, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* B*H*N*N*4 bytes: one float32 score matrix per head. 0 on overflow or bad sizes. */
+size_t fa_naive_workspace_bytes(int B, int H, int N);
+
+/* Static, NUL-terminated name of a status code ("FA_OK", ...). */
+const char* fa_status_str(int status);
+
+/* The hipError_t behind the most recent FA_ERR_HIP on this thread (0 if none). */
+int fa_last_hip_error(void);
+
+/* Frees every decode workspace the library owns (on all devices). Safe to call
+ * more than once; later fa_decode calls allocate again. */
+void fa_shutdown(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

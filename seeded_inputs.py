@@ -142,13 +142,14 @@ def as_float64(x: np.ndarray, dtype: str) -> np.ndarray:
 def random_case(seed: int, B: int, H: int, N: int, d: int, dtype: str, nk: int | None = None, std: float = 1.0):
     """Small ad-hoc case for ragged-shape tests: returns (q, k, v) kernel inputs.
 
-    q is [B,H,N,d]; k, v are [B,H,nk,d] (nk defaults to N). Values are
-    std * N(0,1), cast to bf16 (RNE) for bf16 cases.
+    q is [B,H,N,d]; k, v are [B,H,nk,d] (nk defaults to N). q and k are
+    std * N(0,1) (std sets how peaked the softmax rows are), v is N(0,1);
+    all cast to bf16 (RNE) for bf16 cases.
     """
     nk = N if nk is None else nk
     rng = np.random.Generator(np.random.PCG64([BASE_SEED, 1000 + seed, B, H, N, d, nk]))
     outs = []
-    for rows in (N, nk, nk):
-        x = (rng.standard_normal((B, H, rows, d), dtype=np.float32) * np.float32(std)).astype(np.float32)
+    for rows, sd in ((N, std), (nk, std), (nk, 1.0)):
+        x = (rng.standard_normal((B, H, rows, d), dtype=np.float32) * np.float32(sd)).astype(np.float32)
         outs.append(f32_to_bf16_bits(x) if dtype == "bf16" else x)
     return tuple(outs)

@@ -1,0 +1,150 @@
+"""The C ABI without a GPU: every declared symbol is exported, and argument
+validation rejects bad calls before anything reaches the device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from exact_io_aware_74_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, INVALID, UNSUPPORTED = 0, -1, -2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|size_t|void|const\s+char\s*\*)\s*\**\s*(fa_\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
+              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes"):
+        assert n in names
+    assert len(names) == len(set(names))
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in binding.SIGNATURES, f"binding lacks {name}"
+
+
+# Fake, 16-byte aligned, never dereferenced "device" addresses: validation must
+# fail (or the problem be empty) before any of them is used.
+A = 0x100000
+Bp = 0x200000
+C = 0x300000
+Dp = 0x400000
+L = 0x500000
+
+
+def fwd(lib, *, q=A, k=Bp, v=C, o=Dp, lse=L, B=1, H=1, N=16, d=64, causal=0, scale=0.125, f32=False):
+    fn = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+    return fn(q, k, v, o, lse, B, H, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("f32", [False, True])
+def test_fwd_validation(lib, f32):
+    assert fwd(lib, d=96, f32=f32) == UNSUPPORTED
+    assert fwd(lib, d=32, f32=f32) == UNSUPPORTED
+    assert fwd(lib, d=0, f32=f32) == INVALID
+    assert fwd(lib, q=0, f32=f32) == INVALID
+    assert fwd(lib, o=0, f32=f32) == INVALID
+    assert fwd(lib, k=A + 8, f32=f32) == INVALID                    # misaligned
+    assert fwd(lib, lse=L + 2, f32=f32) == INVALID                  # misaligned lse
+    assert fwd(lib, N=-1, f32=f32) == INVALID
+    assert fwd(lib, B=-3, f32=f32) == INVALID
+    assert fwd(lib, scale=float("nan"), f32=f32) == INVALID
+    assert fwd(lib, scale=float("inf"), f32=f32) == INVALID
+    assert fwd(lib, scale=-0.5, f32=f32) == INVALID
+    assert fwd(lib, o=A, f32=f32) == INVALID                        # output aliases q
+    assert fwd(lib, o=A + 256, f32=f32) == INVALID                  # output overlaps q
+    assert fwd(lib, B=1 << 20, H=1 << 12, N=1 << 12, f32=f32) == INVALID   # grid overflow
+    # empty problems succeed without touching anything (null pointers allowed)
+    assert fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0, f32=f32) == FA_OK
+    assert fwd(lib, N=0, q=0, k=0, v=0, o=0, lse=0, f32=f32) == FA_OK
+    assert fwd(lib, H=0, f32=f32) == FA_OK
+
+
+def test_decode_validation(lib):
+    dec = lambda **kw: lib.fa_decode(kw.get("q", A), kw.get("k", Bp), kw.get("v", C), kw.get("o", Dp),
+                                     kw.get("B", 2), kw.get("H", 2), kw.get("Lkv", 100), kw.get("d", 128),
+                                     kw.get("nsplit", 4), None)
+    assert dec(d=80) == UNSUPPORTED
+    assert dec(Lkv=0) == INVALID
+    assert dec(nsplit=0) == INVALID
+    assert dec(nsplit=-2) == INVALID
+    assert dec(q=0) == INVALID
+    assert dec(v=C + 4) == INVALID
+    assert dec(o=Bp) == INVALID                                      # output inside the K cache
+    assert dec(B=0, q=0, k=0, v=0, o=0) == FA_OK
+
+
+def test_decode_workspace_size(lib):
+    # 16 x 32 heads, 64 splits of 512 keys, (d + 2) floats per split
+    assert lib.fa_decode_workspace_bytes(16, 32, 32768, 128, 64) == 17_039_360
+    # nsplit is clamped to Lkv and empty chunks are dropped: Lkv=10, nsplit=6 -> chunk 2 -> 5 splits
+    assert lib.fa_decode_workspace_bytes(1, 1, 10, 64, 6) == 5 * 66 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 10, 64, 1000) == 10 * 66 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 0, 64, 4) == 0
+
+
+def test_naive_workspace_matches_pages(lib, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "pages_figures.json")))
+    for key in ("score_matrix_t8192", "score_matrix_t16384"):
+        e = g[key]
+        # the ablation keeps S/P in float32: twice the pages' fp16 figure
+        per_head = lib.fa_naive_workspace_bytes(1, 1, e["T"])
+        assert per_head == 2 * e["T"] * e["T"] * e["elem_bytes"]
+        assert lib.fa_naive_workspace_bytes(1, e["heads"], e["T"]) == e["heads"] * per_head
+    assert lib.fa_naive_workspace_bytes(1, 32, 8192) == 8_589_934_592
+    assert lib.fa_naive_workspace_bytes(-1, 1, 4) == 0
+
+
+def test_naive_validation(lib):
+    far = 1 << 36   # tensors far apart so that large N does not make them overlap
+    nv = lambda ws=6 * far, nbytes=1 << 40, N=16, **kw: lib.fa_naive_fwd(
+        far, 2 * far, 3 * far, 4 * far, 5 * far, kw.get("B", 1), kw.get("H", 1), N, kw.get("d", 64), 1, 0.125,
+        ws, nbytes, None)
+    assert nv(ws=0) == INVALID
+    assert nv(nbytes=16 * 16 * 4 - 1) == INVALID
+    assert nv(N=40000) == UNSUPPORTED
+    assert nv(d=256) == UNSUPPORTED
+
+
+def test_status_strings(lib):
+    assert lib.fa_status_str(0) == b"FA_OK"
+    assert lib.fa_status_str(-1) == b"FA_ERR_INVALID_ARG"
+    assert lib.fa_status_str(-2) == b"FA_ERR_UNSUPPORTED"
+    assert lib.fa_status_str(-3) == b"FA_ERR_HIP"
+    assert lib.fa_status_str(-4) == b"FA_ERR_NOMEM"
+    assert lib.fa_status_str(7) == b"FA_ERR_UNKNOWN"
+    assert lib.fa_last_hip_error() == 0
+
+
+def test_binding_errors_are_raised(lib):
+    with pytest.raises(binding.FaError) as ei:
+        binding._check("fa_fwd", UNSUPPORTED)
+    assert "FA_ERR_UNSUPPORTED" in str(ei.value)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The package and its C sources never import, call or link the oracle."""
+    pkg = os.path.join(ROOT, "exact_io_aware_74_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
+    assert "oracle" not in open(HEADER).read().lower()

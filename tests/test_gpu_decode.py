@@ -1,0 +1,100 @@
+"""Parity of split-KV decode (split + combine kernels) with the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from exact_io_aware_74_amd import binding as fa
+from helpers import assert_close, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_case(B, H, L, d, nsplit, seed, std=1.0):
+    q, k, v = si.random_case(seed, B, H, 1, d, "bf16", nk=L, std=std)
+    qd = to_device(q[:, :, 0, :], "bf16")
+    kd, vd = to_device(k, "bf16"), to_device(v, "bf16")
+    o = fa.decode(qd, kd, vd, nsplit=nsplit)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(si.as_float64(q, "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
+    return to_f64(o), ref, (qd, kd, vd)
+
+
+def test_workload_decode_b16h32_l32768_sampled_heads():
+    w = si.WORKLOADS["decode_b16h32_l32768_d128"]
+    q = si.tensor_full(w, "q")[:, :, 0, :]
+    k = si.tensor_full(w, "k")
+    v = si.tensor_full(w, "v")
+    qd, kd, vd = to_device(q, "bf16"), to_device(k, "bf16"), to_device(v, "bf16")
+    o = to_f64(fa.decode(qd, kd, vd, nsplit=w.nsplit))
+    heads = [(0, 0), (3, 5), (7, 31), (8, 16), (12, 1), (15, 31)]
+    got, ref = [], []
+    for b, h in heads:
+        r, _ = oracle.decode(si.as_float64(q[b:b + 1, h:h + 1], "bf16"), si.as_float64(k[b:b + 1, h:h + 1], "bf16"),
+                             si.as_float64(v[b:b + 1, h:h + 1], "bf16"))
+        got.append(o[b, h])
+        ref.append(r[0, 0])
+    print("decode full-size", assert_close(np.stack(got), np.stack(ref), "bf16"))
+    assert np.isfinite(o).all()
+
+
+@pytest.mark.parametrize("nsplit", [1, 2, 7, 64, 999, 1000, 5000])
+def test_nsplit_sweep(nsplit):
+    got, ref, _ = _decode_case(2, 3, 1000, 128, nsplit, seed=11, std=2.0)
+    assert_close(got, ref, "bf16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("L", [1, 2, 17, 333, 4097])
+def test_ragged_cache_lengths(d, L):
+    got, ref, _ = _decode_case(2, 2, L, d, 64, seed=L + d)
+    assert_close(got, ref, "bf16")
+
+
+def test_single_key_returns_v():
+    got, _, (qd, kd, vd) = _decode_case(3, 2, 1, 128, 4, seed=3)
+    np.testing.assert_array_equal(got, to_f64(vd[:, :, 0, :]))
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    B, H, N, d = 2, 4, 515, 128
+    q, k, v = si.random_case(21, B, H, N, d, "bf16")
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o_fwd, _ = fa.fwd(qd, kd, vd, causal=True)
+    o_dec = fa.decode(qd[:, :, N - 1, :].contiguous(), kd, vd, nsplit=8)
+    ref, _ = oracle.decode(si.as_float64(q[:, :, N - 1], "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
+    assert_close(to_f64(o_dec), ref, "bf16")
+    assert_close(to_f64(o_fwd[:, :, N - 1, :]), ref, "bf16")
+
+
+def test_cache_permutation_invariance():
+    B, H, L, d = 1, 2, 700, 64
+    q, k, v = si.random_case(22, B, H, 1, d, "bf16", nk=L)
+    perm = np.random.default_rng(5).permutation(L)
+    qd = to_device(q[:, :, 0, :], "bf16")
+    o1 = to_f64(fa.decode(qd, to_device(k, "bf16"), to_device(v, "bf16"), nsplit=7))
+    o2 = to_f64(fa.decode(qd, to_device(np.ascontiguousarray(k[:, :, perm]), "bf16"),
+                          to_device(np.ascontiguousarray(v[:, :, perm]), "bf16"), nsplit=7))
+    ref, _ = oracle.decode(si.as_float64(q, "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
+    assert_close(o1, ref, "bf16")
+    assert_close(o2, ref, "bf16")
+
+
+def test_workspace_regrows_and_streams():
+    """Small, large, small again on one stream, then on a second stream: all correct."""
+    for L, ns in ((100, 4), (5000, 64), (300, 3)):
+        got, ref, _ = _decode_case(2, 2, L, 128, ns, seed=L)
+        assert_close(got, ref, "bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got, ref, _ = _decode_case(1, 3, 2000, 64, 16, seed=77)
+    s.synchronize()
+    assert_close(got, ref, "bf16")
+
+
+def test_deterministic():
+    _, _, (qd, kd, vd) = _decode_case(2, 2, 3000, 128, 64, seed=9)
+    a = fa.decode(qd, kd, vd, nsplit=64)
+    b = fa.decode(qd, kd, vd, nsplit=64)
+    assert torch.equal(a, b)
