@@ -1,0 +1,201 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one fused causal prefill (B=1, H=32, N=8192, d=128, bf16, K
+doubled) followed by one split-KV decode (B=16, H=32, one query row, a
+32768-key bf16 cache, d=128, 64 splits), both on the same HIP stream, with
+inputs already resident in HBM. After W warm-up steps, exactly K steps are
+timed between two device synchronisations; HIP events recorded on the launch
+stream around each call give the per-call kernel time.
+
+Prints one JSON line: `value` is the prefill's attention-forward throughput
+(algorithmic FLOPs / average prefill time), with a `roofline` entry for the
+fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
+throughput on a bounded sample of the prefill workload in `cpu_baseline`.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) at N=8K d=128; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the published 2.5 PFLOP/s dense)
+PEAK_HBM_GBPS = 8000.0       # published HBM3E bandwidth
+PREFILL = "bf16_h32_n8192_d128_causal_k2"
+DECODE = "decode_b16h32_l32768_d128"
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_n8192.json")
+FWD_SOURCES = [os.path.join(ROOT, "exact_io_aware_74_amd", "csrc", f) for f in ("fa_fwd_bf16.hip", "fa_device.h")]
+
+
+def fwd_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in FWD_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launches_per_record: int = 1):
+    """HBM bytes per fused-kernel launch from the committed counter record, if it
+    was taken on the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_RECORD):
+        return None
+    rec = json.load(open(TRAFFIC_RECORD))
+    if rec.get("kernel_source_digest") != fwd_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle, untuned, on whole heads of the prefill workload until about target_s seconds."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        cores = len(os.sched_getaffinity(0))
+    heads, elapsed, flops = 0, 0.0, 0
+    while elapsed < target_s and heads < w.H:
+        h = heads
+        q, k, v = (si.as_float64(si.tensor_slice(w, t, 0, h), w.dtype)[None, None] for t in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        O, _ = oracle.attention(q, k, v, w.causal, w.scale)
+        elapsed += time.perf_counter() - t0
+        assert np.isfinite(O).all()
+        flops += oracle.attention_flops(1, 1, w.N, w.d, w.causal)
+        heads += 1
+    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} of {w.H} heads of the N=8192 d=128 causal prefill (all rows), fp64 numpy, "
+                      f"{elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                    help="CPU work of the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: launch it without torch.distributed", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    from exact_io_aware_74_amd import binding as fa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
+    t_gen = time.perf_counter()
+    q, k, v = (to_dev(si.tensor_full(wp, t)) for t in ("q", "k", "v"))
+    dq = to_dev(si.tensor_full(wd, "q")[:, :, 0, :])
+    dk = to_dev(si.tensor_full(wd, "k"))
+    dv = to_dev(si.tensor_full(wd, "v"))
+    gen_s = time.perf_counter() - t_gen
+    o = torch.empty_like(q)
+    lse = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+    do = torch.empty_like(dq)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)    # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.fwd(q, k, v, causal=True, scale=wp.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        fa.decode(dq, dk, dv, nsplit=wd.nsplit, out=do)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert torch.isfinite(o).all().item() and torch.isfinite(do.float()).all().item()
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    flops = 4 * wp.d * wp.B * wp.H * (wp.N * (wp.N + 1) // 2)            # 4 d per visible (query, key) pair
+    fwd_bytes = 4 * wp.B * wp.H * wp.N * wp.d * 2 + wp.B * wp.H * wp.N * 4  # Q, K, V, O + LSE
+    tflops = flops / (fwd_avg * 1e-3) / 1e12
+    dec_bytes = 2 * wd.B * wd.H * wd.Lkv * wd.d * 2 + 2 * wd.B * wd.H * wd.d * 2  # K, V caches + q, o
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=1 H=32 N=8192 d=128 bf16 causal, K x2 (value); "
+                               "decode B=16 H=32 Lkv=32768 d=128 bf16 nsplit=64 (decode)",
+                   "prefill": {"B": wp.B, "H": wp.H, "N": wp.N, "d": wp.d, "causal": True, "scale": wp.scale},
+                   "decode": {"B": wd.B, "H": wd.H, "Lkv": wd.Lkv, "d": wd.d, "nsplit": wd.nsplit}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                     "kernel": "fwd_bf16_kernel<128, causal>", "algorithmic_flop_per_launch": flops,
+                     "kernel_ms": round(fwd_avg, 4)},
+        "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                "algorithmic_bytes_per_call": dec_bytes,
+                                "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>",
+                                "ms": round(dec_avg, 4)}},
+        "prefill": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), "ms_max": round(max(fwd_ms), 4),
+                    "compulsory_bytes": fwd_bytes},
+        "input_generation_s": round(gen_s, 1),
+    }
+    del q, k, v, dq, dk, dv, o, do
+    if args.cpu_baseline_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(wp, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
