@@ -33,10 +33,17 @@ def _run(cmd):
     return out
 
 
+# Per-source extra flags. The fused forward keeps O^T in AGPRs through inline
+# asm and wants the compiler's own MFMAs (the scores, read by the softmax) in
+# VGPRs; its copy asm sets M0, which no other instruction of that kernel uses
+# (the warning about clobbering a reserved register is silenced).
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    _run([HIPCC, *COMMON, *DEVICE_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+    _run([HIPCC, *COMMON, *DEVICE_FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 

@@ -13,6 +13,8 @@
 //  * ds_read_b64_tr_b16, within each group of 16 lanes: lane t receives,
 //    as its element e (e = 0..3), the 16-bit value at position (t % 4) of the
 //    8-byte chunk addressed by lane 4*e + t/4 of its group.
+//  * global_load_lds_dwordx4: lane l's 16 bytes land at the (wave-uniform)
+//    LDS destination + 16*l, whatever global address the lane supplied.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -47,6 +49,46 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p));
 }
+
+// O^T-style accumulation with the accumulator pinned in AGPRs. The compiler
+// does not see inside the asm, so the hazards it would otherwise pad are
+// handled here: `s_nop 1` gives the two wait states a VALU write of an
+// operand (the bf16 probabilities) needs before the matrix core reads it.
+// Back-to-back MFMAs on the same accumulator need no padding.
+__device__ __forceinline__ void mfma32x32x16_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Orders all later accesses to `acc` after this point and, with WAIT, first
+// gives the 19 wait states an MFMA result needs before VALU instructions
+// (v_accvgpr_read/write) may read or overwrite it.
+template <bool WAIT>
+__device__ __forceinline__ void agpr_fence(f32x16& acc) {
+  if constexpr (WAIT)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(acc));
+  else
+    asm volatile("" : "+a"(acc));
+}
+
+// 16-byte copy global -> LDS without a VGPR round trip: lane l's 16 bytes
+// land at LDS byte address `lds_addr` + 16*l (`lds_addr` wave-uniform). Issued
+// through asm so the compiler does not tie later LDS reads to its completion
+// (it cannot tell the ring slots apart and would wait for every copy): the
+// caller must wait for them (wait_vmcnt) before a barrier that publishes the
+// data.
+__device__ __forceinline__ void global_load_lds16(const void* src, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
+}
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave remain
+// outstanding (loads complete in issue order). Issued through the builtin so
+// the compiler accounts for it in its own waits.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0xF70 | (N & 15) | ((N >> 4) << 14));
+}
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(FA_LDS const void*)p; }
 
 // Reductions over the lane pair (l, l ^ 32). v_permlane32_swap on (x, x)
 // returns, in lanes 0..31, (x[l], x[l+32]) and in lanes 32..63,

@@ -1,29 +1,47 @@
 // Fused exact attention forward, bf16 in/out, fp32 accumulation, gfx950.
 //
-// One workgroup owns BR = 128 query rows of one (b, h) head (4 waves x 32
-// rows) and walks the key/value tiles of BC = 64 rows once, keeping the
-// scores on chip: the tiling and online-softmax method of "Describe Flash
-// Attention at a high level" (mantramindai.in), section "The two ideas", and
-// of "How FlashAttention Speeds Up the Attention Layer" (hassanahmed.net),
-// sections on tiling and on the online softmax.
+// The method is the tiling + online-softmax pass of "Describe Flash Attention
+// at a high level" (mantramindai.in), section "The two ideas", and of "How
+// FlashAttention Speeds Up the Attention Layer" (hassanahmed.net), sections on
+// tiling and on the online softmax: each workgroup owns a block of query rows,
+// streams the key/value tiles of its head through on-chip memory once, keeps
+// the scores in registers, and rescales its running sum and output whenever the
+// running row maximum is raised. The N x N score matrix never leaves the chip.
 //
-// Register plumbing (lane layouts in fa_device.h):
-//  * each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, K tile
-//    rows as the A operand (from LDS), its 32 query rows as the B operand
-//    (held in VGPRs for the whole pass). In the S^T accumulator lane l holds
-//    query (l % 32) and 16 keys per 32-key block, so the row max and row sum
-//    are in-lane reductions plus one exchange with lane l ^ 32;
-//  * the same registers, rounded to bf16, are directly the B operand of
-//    O^T += V^T P^T: accumulator element r of lane l is key
-//    (r%4) + 8*(r/4) + 4*(l/32) of its block, and the V^T A operand is read
-//    from the row-major V tile with the transposing LDS read so that its
-//    k-slots hold exactly those keys;
-//  * O^T stays in 4 x 16 accumulators per lane (d = 128), lane l owning query
-//    (l % 32), so the per-row rescale by exp(m_old - m_new) is a per-lane
-//    scalar multiply.
-// Causal: key tiles past the workgroup's last query are never loaded, tiles
-// past a wave's last query are skipped by that wave, and only tiles that
-// straddle the diagonal (or the ragged end of N) evaluate the mask.
+// Mapping onto CDNA4 (lane layouts in fa_device.h):
+//  * one workgroup = 4 waves (one per SIMD) x 64 query rows = 256 rows of one
+//    (b, h) head. A wave holds its rows as two 32-row MFMA blocks, so every K
+//    or V fragment it reads from LDS feeds two v_mfma_f32_32x32x16_bf16;
+//  * scores are computed transposed, S^T = K Q^T, with K rows as the A operand
+//    (LDS) and the wave's queries as the B operand (VGPRs, loaded once). In the
+//    accumulator lane l owns query l % 32 and 16 keys of a 32-key block, so row
+//    max and row sum are in-lane reductions plus one v_permlane32_swap. S is
+//    accumulated in VGPRs, where the softmax reads it;
+//  * the same registers, rounded to bf16, are the B operand of O^T += V^T P^T;
+//    V^T comes from the V tile through the transposing LDS read. O^T stays in
+//    AGPRs for the whole pass;
+//  * K/V tiles of 64 keys are copied HBM -> LDS by global_load_lds_dwordx4
+//    (no VGPR staging) into a 4-deep ring, up to three tiles ahead, one
+//    barrier per tile. The LDS
+//    layouts are blocked so that every read is a per-lane base plus an
+//    immediate and free of bank conflicts: K as [16-byte chunk][key] (a K
+//    fragment read is 256 contiguous bytes per 16 lanes), V as [16-dim
+//    group][key][16 dims] with a 128-byte pad between groups (a transposing
+//    read covers all 64 banks once per 32 lanes);
+//  * software pipeline over 32-key sub-tiles: in one basic block the wave
+//    turns sub-tile t's scores into probabilities and accumulates P V for t
+//    while the MFMAs for S(t+1) run, so softmax VALU work overlaps matrix-core
+//    time;
+//  * the running maximum is only raised when a sub-tile exceeds it by more
+//    than 2^8 in exp2 units (probabilities then stay <= 256: exact in fp32,
+//    representable in bf16). Rows that do not need it keep the old reference,
+//    which leaves O and the log-sum-exp unchanged mathematically, so the O
+//    rescale (an AGPR round trip) is rare and sits on a wave-uniform branch,
+//    as does the causal / ragged-tail mask;
+//  * causal: key tiles past the workgroup's last query are never loaded and
+//    sub-tiles past a wave's last query are skipped by that wave;
+//  * heaviest causal query tiles are dispatched first, and consecutive
+//    workgroups take consecutive heads so a head's K/V stays in one XCD's L2.
 #include <float.h>
 
 #include "fa_device.h"
@@ -31,34 +49,67 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int QB>
 struct FwdTile {
-  static constexpr int NW = 4;                 // waves per workgroup
-  static constexpr int BR = 32 * NW;           // query rows per workgroup
-  static constexpr int BC = 64;                // keys per tile
-  static constexpr int KP = D + 8;             // LDS pitch of a K row, bf16 elements (16 B pad)
-  static constexpr int VP = D + 32;            // LDS pitch of a V row (64 B pad)
-  static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int LOADS = BC * CH / (64 * NW);  // chunks per thread per tensor per tile
-  static_assert(LOADS * 64 * NW == BC * CH, "tile must split evenly over the threads");
+  static constexpr int NW = 8 / QB;             // waves per workgroup
+  static constexpr int WR = 32 * QB;            // query rows per wave (QB MFMA blocks of 32)
+  static constexpr int BR = NW * WR;            // query rows per workgroup
+  static constexpr int BC = 64;                 // keys per LDS tile (two 32-key sub-tiles)
+  static constexpr int NBUF = 4;                // LDS ring depth
+  static constexpr int CH = D / 8;              // 16-byte chunks per row
+  static constexpr int NC = D / 16;             // 16-deep k-chunks of the QK product
+  static constexpr int NDB = D / 32;            // 32-wide head-dim blocks of O
+  static constexpr int NG = D / 16;             // 16-dim groups of the V layout
+  static constexpr int GSTRIDE = BC * 32 + 128; // bytes per V group (64 keys x 32 B + pad)
+  static constexpr int KBYTES = CH * BC * 16;   // K tile bytes: [chunk][key][16 B]
+  static constexpr int VBYTES = NG * GSTRIDE;   // V tile bytes
+  static constexpr int SLOT = KBYTES + VBYTES;  // one ring slot
+  static constexpr int IPW = CH / NW;           // DMA instructions per wave per tensor per tile
+  static_assert(IPW * NW == CH && 2 * NG == CH, "DMA split");
+  static_assert(NBUF * SLOT <= 163840, "LDS budget");
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+// O^T += V^T P^T for one 32x32 block. With one query block per wave O^T
+// (64 registers at d = 128) lives in VGPRs next to everything else and the
+// compiler's MFMA is used; with two blocks O^T needs 128 registers and is
+// pinned in AGPRs through asm (the scores stay in VGPRs for the softmax).
+template <int QB>
+__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& v, const bf16x8& p) {
+  if constexpr (QB == 1)
+    acc = mfma32x32x16(v, p, acc);
+  else
+    mfma32x32x16_agpr(acc, v, p);
+}
+// Makes the O^T accumulators safe to touch with VALU instructions (only the
+// AGPR variant needs the explicit wait states).
+template <int QB, int NDB>
+__device__ __forceinline__ void o_fence(f32x16 (&oacc)[QB][NDB]) {
+  if constexpr (QB > 1) {
+    agpr_fence<true>(oacc[0][0]);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        if (qb + db > 0) agpr_fence<false>(oacc[qb][db]);
+  }
+}
+
+// Threshold (exp2 units) by which a sub-tile maximum must exceed the running
+// reference before the reference is raised and O rescaled.
+constexpr float kRescaleThreshold = 8.f;
+
+template <int D, int QB, bool CAUSAL>
+__global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
                                                           uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                          int N, float scale, int n_qt, int BH) {
-  using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[T::BC * T::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[T::BC * T::VP];
+                                                          int N, float scale, float c2, int n_qt, int BH) {
+  using T = FwdTile<D, QB>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NBUF * T::SLOT];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, hf = l >> 5, lq = l & 31;
-  // Consecutive workgroups take consecutive heads of the same query-tile rank,
-  // so with B*H a multiple of 8 every head stays on one XCD (workgroups are
-  // dealt round-robin over the 8 XCDs) and its K/V tiles are shared in that
-  // XCD's L2. Causal: the heaviest query tiles are dispatched first.
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: scalar branches below
+  const int l = tid & 63, hf = l >> 5, lq = l & 31;
   const int bh = blockIdx.x % BH;
   const int rank = blockIdx.x / BH;
   const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
@@ -67,175 +118,357 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const uint16_t* __rest
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
-  const int wq0 = q0 + 32 * w;          // first query row of this wave
-  const int qrow = wq0 + lq;            // the query row this lane owns
+  const int wq0 = q0 + T::WR * w;  // first query row of this wave
 
-  // Q^T as the B operand: k-slots of chunk c are head dims 16c + 8*hf + (0..7).
-  bf16x8 qop[D / 16];
+  // ---- DMA of one K/V tile into a ring slot; wave w copies K chunks and V
+  // group halves w*IPW .. w*IPW + IPW - 1 ----
+  auto dma = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint32_t kb = lds_addr(lds) + slot * T::SLOT;
+    const uint32_t vb = kb + T::KBYTES;
+    const int k0 = j * T::BC;
+    const uint16_t* krow = Kh + (size_t)min(k0 + l, N - 1) * D;  // keys past N: any valid row, masked later
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (qrow < N)
-      qop[c] = *(const bf16x8*)(Qh + (size_t)qrow * D + 16 * c + 8 * hf);
-    else
-      qop[c] = (bf16x8){};
-  }
-
-  const float c2 = scale * kLog2e;      // logits in base-2 units: exp(scale*x) = exp2(c2*x)
-  float m = -FLT_MAX;                   // running max of the raw scores q.k
-  float lsum = 0.f;                     // this half-wave's share of the running sum
-  f32x16 oacc[D / 32];
+    for (int i = 0; i < T::IPW; ++i) {
+      const int c = w * T::IPW + i;  // K: chunk c of keys k0 .. k0 + 63
+      global_load_lds16(krow + 8 * c, kb + c * 1024);
+    }
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i) oacc[i] = (f32x16){};
+    for (int i = 0; i < T::IPW; ++i) {
+      const int v = w * T::IPW + i;  // V: group v / 2, keys k0 + 32 * (v % 2) .. + 31
+      const int key = min(k0 + 32 * (v & 1) + (l >> 1), N - 1);
+      global_load_lds16(Vh + (size_t)key * D + 16 * (v >> 1) + 8 * (l & 1),
+                        vb + (v >> 1) * T::GSTRIDE + (v & 1) * 1024);
+    }
+  };
 
   const int kv_end = CAUSAL ? min(N, q0 + T::BR) : N;
   const int n_kt = (kv_end + T::BC - 1) / T::BC;
+  // 32-key sub-tiles this wave computes (0 for a wave entirely past N)
+  const int wv_end = CAUSAL ? min(N, wq0 + T::WR) : N;
+  const int n_st = wq0 < N ? (wv_end + 31) / 32 : 0;
 
-  u32x4 kst[T::LOADS], vst[T::LOADS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = tid + 64 * T::NW * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      const int key = kt * T::BC + row;
-      if (key < N) {
-        kst[i] = *(const u32x4*)(Kh + (size_t)key * D + ch * 8);
-        vst[i] = *(const u32x4*)(Vh + (size_t)key * D + ch * 8);
-      } else {  // rows past N are zero so that 0 * V stays finite
-        kst[i] = (u32x4){};
-        vst[i] = (u32x4){};
-      }
-    }
-  };
-  auto lstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int idx = tid + 64 * T::NW * i;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      *(u32x4*)(k_lds + row * T::KP + ch * 8) = kst[i];
-      *(u32x4*)(v_lds + row * T::VP + ch * 8) = vst[i];
-    }
-  };
+  dma(0, 0);
+  if (n_kt > 1) dma(1, 1);
 
-  // Source address of this lane in the transposing V reads: lane (g, s) of
-  // 16-lane group g serves key 4*(g/2) + s/4 (+16*kc, +8 for the second read)
-  // and head dims 16*(g%2) + 4*(s%4) .. +3 (+32*db).
+  // ---- Q^T as the B operand: k-slots of chunk c are head dims 16c + 8*hf + (0..7) ----
+  bf16x8 qop[QB][T::NC];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wq0 + 32 * qb + lq;
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+      if (row < N)
+        qop[qb][c] = *(const bf16x8*)(Qh + (size_t)row * D + 16 * c + 8 * hf);
+      else
+        qop[qb][c] = (bf16x8){};
+    }
+  }
+
+  // Per-lane LDS byte offsets within a slot. K fragment (A operand): key lq
+  // of the sub-tile, chunk 2c + hf. V^T fragment (transposing read): lane
+  // (g, s) of 16-lane group g addresses key 4*(g/2) + s/4 (+8 for the second
+  // half) and head dims 16*(g%2) + 4*(s%4) (+32 per head-dim block).
   const int g16 = l >> 4, s16 = l & 15;
-  const int v_src = (4 * (g16 >> 1) + (s16 >> 2)) * T::VP + 16 * (g16 & 1) + 4 * (s16 & 3);
+  const int k_lane = hf * 1024 + lq * 16;
+  const int v_lane = T::KBYTES + (g16 & 1) * T::GSTRIDE + (4 * (g16 >> 1) + (s16 >> 2)) * 32 + 8 * (s16 & 3);
 
-  const bool wave_has_rows = wq0 < N;
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt) gload(kt + 1);   // next tile's loads fly while this one is used
-    const int k0 = kt * T::BC;
-    const bool active = wave_has_rows && (!CAUSAL || k0 <= wq0 + 31);
-    if (active) {
-      // ---- S^T = K Q^T for BC keys x 32 queries ----
-      f32x16 sacc[T::BC / 32];
+  f32x16 sA[QB], sB[QB];    // S^T of one 32-key sub-tile per query block (VGPRs)
+  f32x16 oacc[QB][T::NDB];  // O^T (AGPRs): lane l owns query l % 32 of each block
+  float m[QB];              // reference maximum of the raw scores q.k
+  float lsum[QB];           // this half-wave's share of the running sum
+  float mt[QB];             // maximum of the pending sub-tile
 #pragma unroll
-      for (int kb = 0; kb < T::BC / 32; ++kb) {
-        sacc[kb] = (f32x16){};
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 a = *(const bf16x8*)(k_lds + (32 * kb + lq) * T::KP + 16 * c + 8 * hf);
-          sacc[kb] = mfma32x32x16(a, qop[c], sacc[kb]);
-        }
-      }
-      // ---- mask (only tiles that reach past N or cross the diagonal) ----
-      const bool need_mask = (k0 + T::BC > N) || (CAUSAL && k0 + T::BC - 1 > wq0);
-      if (need_mask) {
+    for (int db = 0; db < T::NDB; ++db) oacc[qb][db] = (f32x16){};
+    m[qb] = -INFINITY;
+    lsum[qb] = 0.f;
+  }
+
+  // S^T for the 32-key half h of the tile whose K sits at k_addr
+  auto qk = [&](f32x16(&s)[QB], int k_addr, int h) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < T::BC / 32; ++kb)
+    for (int c = 0; c < T::NC; ++c) {
+      const bf16x8 a = *(const bf16x8*)(lds + k_addr + (c * 2048 + h * 512));
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + (r & 3) + 8 * (r >> 2) + 4 * hf;
-            const bool vis = key < N && (!CAUSAL || key <= qrow);
-            if (!vis) sacc[kb][r] = -INFINITY;
-          }
-      }
-      // ---- online softmax update ----
-      float mt = -INFINITY;
+      for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qop[qb][c], c == 0 ? (f32x16){} : s[qb]);
+    }
+  };
+  auto tile_max = [&](const f32x16(&s)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < T::BC / 32; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      float x = s[qb][0];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
-      mt = halves_max(mt);
-      const float m_new = fmaxf(m, mt);
-      const float alpha = fast_exp2((m - m_new) * c2);
-      const float mc = m_new * c2;
-      m = m_new;
-      float ps = 0.f;
+      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[qb][r]);
+      mt[qb] = halves_max(x);
+    }
+  };
+  // keys past N and (causal) keys after the query row get -inf
+  auto needs_mask = [&](int t) __attribute__((always_inline)) {
+    return (32 * t + 32 > N) || (CAUSAL && 32 * t + 31 > wq0);
+  };
+  auto mask = [&](f32x16(&s)[QB], int t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < T::BC / 32; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = wq0 + 32 * qb + lq;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(sacc[kb][r], c2, -mc));
-          if (need_mask && sacc[kb][r] == -INFINITY) p = 0.f;  // also right when scale == 0
-          sacc[kb][r] = p;
-          ps += p;
-        }
-      lsum = alpha * lsum + ps;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int kc = 0; kc < T::BC / 16; ++kc) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 two = to_bf16x2(sacc[kc >> 1][8 * (kc & 1) + e], sacc[kc >> 1][8 * (kc & 1) + e + 1]);
-          pb[e] = two[0];
-          pb[e + 1] = two[1];
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const uint16_t* src = v_lds + v_src + 16 * kc * T::VP + 32 * db;
-          const s16x4 lo = lds_read_tr16(src);
-          const s16x4 hi = lds_read_tr16(src + 8 * T::VP);
-          const s16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb, oacc[db]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
+        const bool vis = key < N && (!CAUSAL || key <= qrow);
+        if (!vis) s[qb][r] = -INFINITY;
       }
     }
+  };
+  // Raise the reference maximum where a row's new sub-tile exceeds it by more
+  // than the threshold (wave-uniform branch; every lane then takes the exact
+  // online-softmax update, with alpha = 1 where its maximum did not move).
+  auto maybe_rescale = [&]() __attribute__((always_inline)) {
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) need = need || (mt[qb] - m[qb]) * c2 > kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      o_fence(oacc);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_new = fmaxf(m[qb], mt[qb]);
+        const float alpha = fast_exp2((m[qb] - m_new) * c2);
+        m[qb] = m_new;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+      }
+    }
+  };
+  // Probabilities of a sub-tile against the reference maximum: bf16 B operand
+  // of P V and this half-wave's fp32 row sums. One call handles elements r,
+  // r + 1 of query block qb (mc = reference maximum in exp2 units).
+  auto prob_pair = [&](const f32x16(&s)[QB], bf16x8(&pb)[QB][2], float(&ps)[QB], const float(&mc)[QB], int qb,
+                       int r) __attribute__((always_inline)) {
+    const float p0 = fast_exp2(fmaf(s[qb][r], c2, -mc[qb]));
+    const float p1 = fast_exp2(fmaf(s[qb][r + 1], c2, -mc[qb]));
+    ps[qb] += p0 + p1;
+    const bf16x2 two = to_bf16x2(p0, p1);
+    // pins the pair's arithmetic before the next scheduling fence (pure
+    // arithmetic would otherwise sink next to its use in the P V MFMAs)
+    asm volatile("" ::"v"(two), "v"(ps[qb]));
+    pb[qb][r >> 3][r & 7] = two[0];
+    pb[qb][r >> 3][(r & 7) + 1] = two[1];
+  };
+  // element pairs in the order P V consumes them: 16-key chunk, block, element
+  constexpr int NPAIR = 8 * QB;
+  auto pair_qb = [](int i) { return (i >> 2) % QB; };
+  auto pair_r = [](int i) { return 8 * (i / (4 * QB)) + 2 * (i & 3); };
+  // K fragments (A operand of S^T) of 32-key half h of the tile at k_addr
+  auto load_k = [&](bf16x8(&kf)[T::NC], int k_addr, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(lds + k_addr + (c * 2048 + h * 512));
+  };
+  // V^T fragment (A operand of O^T) for 16-key chunk kc and head-dim block db
+  // of 32-key half h of the tile at v_addr
+  auto load_v = [&](int v_addr, int h, int kc, int db) __attribute__((always_inline)) {
+    const uint8_t* src = lds + v_addr + (db * 2 * T::GSTRIDE + (32 * h + 16 * kc) * 32);
+    const s16x4 lo = lds_read_tr16(src);
+    const s16x4 hi = lds_read_tr16(src + 8 * 32);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  bf16x8 kf[T::NC];  // K fragments of the next sub-tile to score (loaded one step ahead)
+
+  // One pipeline step: finish sub-tile t (its V at v_addr, half t % 2), score
+  // sub-tile t + 1 (its K already in kf; needs t + 1 < n_st) and fetch the K
+  // fragments of sub-tile t + 2 (half t % 2 of the tile at kp_addr). The
+  // instruction order is pinned by scheduling fences so that the matrix core
+  // has work queued at every point: first the score MFMAs of t + 1, each
+  // k-chunk followed by some probabilities of t and one V^T fragment read;
+  // then the P V MFMAs of t, each head-dim block followed by the last
+  // probabilities (first half), a slice of the row maximum of t + 1 and part
+  // of the next K fragments.
+  auto step_body = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+                       __attribute__((always_inline)) {
+    const int h = t & 1;
+    bf16x8 vf[2][T::NDB], pb[QB][2];
+    float ps[QB], mc[QB], mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ps[qb] = 0.f;
+      mc[qb] = m[qb] * c2;
+      mx[qb] = -INFINITY;
+    }
+    constexpr int EARLY = 3 * NPAIR / 4;  // pairs computed under the score MFMAs
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) nxt[qb] = mfma32x32x16(kf[c], qop[qb][c], c == 0 ? (f32x16){} : nxt[qb]);
+#pragma unroll
+      for (int i = EARLY * c / T::NC; i < EARLY * (c + 1) / T::NC; ++i)
+        prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
+      vf[c / T::NDB][c % T::NDB] = load_v(v_addr, h, c / T::NDB, c % T::NDB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int PER = 16 / (2 * T::NDB);  // max elements per query block per head-dim block
+#pragma unroll
+    for (int i = 0; i < 2 * T::NDB; ++i) {
+      const int kc = i / T::NDB, db = i % T::NDB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], vf[kc][db], pb[qb][kc]);
+      if (i < T::NDB) {
+#pragma unroll
+        for (int p = EARLY + (NPAIR - EARLY) * i / T::NDB; p < EARLY + (NPAIR - EARLY) * (i + 1) / T::NDB; ++p)
+          prob_pair(cur, pb, ps, mc, pair_qb(p), pair_r(p));
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) mx[qb] = fmaxf(mx[qb], nxt[qb][i * PER + e]);
+#pragma unroll
+      for (int c = i * T::NC / (2 * T::NDB); c < (i + 1) * T::NC / (2 * T::NDB); ++c)
+        kf[c] = *(const bf16x8*)(lds + kp_addr + (c * 2048 + h * 512));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      lsum[qb] += ps[qb];
+      mt[qb] = halves_max(mx[qb]);
+    }
+  };
+  // the same when sub-tile t + 1 is known to be fully visible
+  auto clean_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+                        __attribute__((always_inline)) {
+    step_body(cur, nxt, t, v_addr, kp_addr);
+    maybe_rescale();
+  };
+  auto full_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+                       __attribute__((always_inline)) {
+    step_body(cur, nxt, t, v_addr, kp_addr);
+    if (needs_mask(t + 1)) {
+      mask(nxt, t + 1);
+      tile_max(nxt);
+    }
+    maybe_rescale();
+  };
+  // the wave's last sub-tile: probabilities and P V only
+  auto last_step = [&](f32x16(&cur)[QB], int t, int v_addr) __attribute__((always_inline)) {
+    bf16x8 pb[QB][2];
+    float ps[QB], mc[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      ps[qb] = 0.f;
+      mc[qb] = m[qb] * c2;
+    }
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        const bf16x8 a = load_v(v_addr, t & 1, kc, db);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], a, pb[qb][kc]);
+      }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
+  };
+  auto tail_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+                       __attribute__((always_inline)) {
+    if (t + 1 < n_st)
+      full_step(cur, nxt, t, v_addr, kp_addr);
+    else if (t < n_st)
+      last_step(cur, t, v_addr);
+  };
+  // End of tile j: tile j + 2 resident for every wave (its K is fetched from
+  // the next step on) and every wave done with tile j, whose ring slot then
+  // receives tile j + 4. A wave's copies complete in issue order, so with
+  // tile j + 3 also in flight it waits until only that tile's copies remain.
+  auto end_tile = [&](int j) __attribute__((always_inline)) {
+    if (j + 3 < n_kt)
+      wait_vmcnt<2 * T::IPW>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
-    if (kt + 1 < n_kt) {
-      lstore();
-      __syncthreads();
-    }
+    if (j + 4 < n_kt) dma(j + 4, j & 3);
+  };
+
+  wait_vmcnt<0>();  // Q, tiles 0 and 1
+  __syncthreads();
+  if (n_kt > 2) dma(2, 2);
+  if (n_kt > 3) dma(3, 3);
+  if (n_st > 0) {
+    qk(sA, k_lane, 0);
+    if (needs_mask(0)) mask(sA, 0);
+    tile_max(sA);
+    maybe_rescale();
+  }
+  load_k(kf, k_lane, 1);  // sub-tile 1 (tile 0, second half)
+  // Leading sub-tiles that need no mask: the steady-state loop runs the tiles
+  // whose both steps start such a sub-tile, with no branch but the rare
+  // rescale; the remaining tiles (diagonal, ragged end, or waves that are
+  // done and only help with the copies) go through the general step. Tile j
+  // sits in ring slot j % 4. Steps past a wave's last sub-tile fetch unused
+  // (in-range) K fragments.
+  const int n_clean = min(CAUSAL ? (wq0 + 1) / 32 : N / 32, N / 32);
+  const int j_clean = max(0, (n_clean - 1) / 2);
+  int j = 0;
+  for (; j < j_clean; ++j) {
+    const int s0 = (j & 3) * T::SLOT, s1 = ((j + 1) & 3) * T::SLOT;
+    clean_step(sA, sB, 2 * j, s0 + v_lane, s1 + k_lane);
+    clean_step(sB, sA, 2 * j + 1, s0 + v_lane, s1 + k_lane);
+    end_tile(j);
+  }
+  for (; j < n_kt; ++j) {
+    const int s0 = (j & 3) * T::SLOT, s1 = ((j + 1) & 3) * T::SLOT;
+    tail_step(sA, sB, 2 * j, s0 + v_lane, s1 + k_lane);
+    tail_step(sB, sA, 2 * j + 1, s0 + v_lane, s1 + k_lane);
+    end_tile(j);
   }
 
   // ---- epilogue: O = acc / l, one rounding to bf16; LSE in natural log ----
-  const float ltot = halves_sum(lsum);
-  if (qrow < N) {
-    const float inv = 1.f / ltot;
-    uint16_t* orow = O + head + (size_t)qrow * D;
+  o_fence(oacc);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float ltot = halves_sum(lsum[qb]);
+    const int qrow = wq0 + 32 * qb + lq;
+    if (qrow < N) {
+      const float inv = 1.f / ltot;
+      uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const bf16x2 a = to_bf16x2(oacc[db][4 * rb] * inv, oacc[db][4 * rb + 1] * inv);
-        const bf16x2 b = to_bf16x2(oacc[db][4 * rb + 2] * inv, oacc[db][4 * rb + 3] * inv);
-        const bf16x4 four = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-        *(bf16x4*)(orow + 32 * db + 8 * rb + 4 * hf) = four;
-      }
-    if (LSE != nullptr && hf == 0) LSE[(size_t)bh * N + qrow] = m * scale + __logf(ltot);
+      for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const bf16x2 a = to_bf16x2(oacc[qb][db][4 * rb] * inv, oacc[qb][db][4 * rb + 1] * inv);
+          const bf16x2 b = to_bf16x2(oacc[qb][db][4 * rb + 2] * inv, oacc[qb][db][4 * rb + 3] * inv);
+          const bf16x4 four = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+          *(bf16x4*)(orow + 32 * db + 8 * rb + 4 * hf) = four;
+        }
+      if (LSE != nullptr && hf == 0) LSE[(size_t)bh * N + qrow] = m[qb] * scale + __logf(ltot);
+    }
   }
 }
+
+#ifndef FA_FWD_QB
+#define FA_FWD_QB 1
+#endif
+// query blocks of 32 rows per wave: 1 = eight waves (two per SIMD, the
+// hardware interleaves them), 2 = four waves with every LDS fragment feeding
+// two MFMAs
+constexpr int kFwdQB = FA_FWD_QB;
 
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                     int N, float scale, hipStream_t s) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, kFwdQB>;
   const int n_qt = (N + T::BR - 1) / T::BR;
   const int BH = B * H;
+  // exp2 units; a positive floor keeps masked (-inf) scores at probability 0
+  // when scale is 0 (every visible probability is then exp2(~0) = 1)
+  float c2 = scale * kLog2e;
+  if (!(c2 >= FLT_MIN)) c2 = FLT_MIN;
   dim3 grid((unsigned)(n_qt * BH)), block(64 * T::NW);
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)o;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &scale, (void*)&n_qt, (void*)&BH};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, CAUSAL>, grid, block, args, 0, s);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &scale, &c2, (void*)&n_qt, (void*)&BH};
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, kFwdQB, CAUSAL>, grid, block, args, 0, s);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
