@@ -9,35 +9,33 @@
 // running row maximum is raised. The N x N score matrix never leaves the chip.
 //
 // Mapping onto CDNA4 (lane layouts in fa_device.h):
-//  * one workgroup = 4 waves (one per SIMD) x 64 query rows = 256 rows of one
-//    (b, h) head. A wave holds its rows as two 32-row MFMA blocks, so every K
-//    or V fragment it reads from LDS feeds two v_mfma_f32_32x32x16_bf16;
+//  * one workgroup = 8 waves (two per SIMD) x 32 query rows = 256 rows of one
+//    (b, h) head (the code also builds a 4-wave variant with 64 rows per
+//    wave, see kFwdQB);
 //  * scores are computed transposed, S^T = K Q^T, with K rows as the A operand
 //    (LDS) and the wave's queries as the B operand (VGPRs, loaded once). In the
 //    accumulator lane l owns query l % 32 and 16 keys of a 32-key block, so row
 //    max and row sum are in-lane reductions plus one v_permlane32_swap. S is
 //    accumulated in VGPRs, where the softmax reads it;
 //  * the same registers, rounded to bf16, are the B operand of O^T += V^T P^T;
-//    V^T comes from the V tile through the transposing LDS read. O^T stays in
-//    AGPRs for the whole pass;
+//    V^T comes from the V tile through the transposing LDS read;
 //  * K/V tiles of 64 keys are copied HBM -> LDS by global_load_lds_dwordx4
 //    (no VGPR staging) into a 4-deep ring, up to three tiles ahead, one
-//    barrier per tile. The LDS
-//    layouts are blocked so that every read is a per-lane base plus an
-//    immediate and free of bank conflicts: K as [16-byte chunk][key] (a K
-//    fragment read is 256 contiguous bytes per 16 lanes), V as [16-dim
-//    group][key][16 dims] with a 128-byte pad between groups (a transposing
-//    read covers all 64 banks once per 32 lanes);
+//    barrier per tile. Tiles are row-major by 64-dim octets (one copy
+//    instruction moves 8 keys x 128 contiguous bytes) with the 16-byte chunks
+//    XOR-swizzled per key, so K fragment reads and transposing V reads are
+//    free of bank conflicts and every read address is one of a few per-lane
+//    bases plus an immediate;
 //  * software pipeline over 32-key sub-tiles: in one basic block the wave
 //    turns sub-tile t's scores into probabilities and accumulates P V for t
-//    while the MFMAs for S(t+1) run, so softmax VALU work overlaps matrix-core
-//    time;
+//    while the MFMAs for S(t+1) run; with two waves per SIMD the hardware
+//    also overlaps one wave's softmax with the other's MFMAs;
 //  * the running maximum is only raised when a sub-tile exceeds it by more
 //    than 2^8 in exp2 units (probabilities then stay <= 256: exact in fp32,
 //    representable in bf16). Rows that do not need it keep the old reference,
 //    which leaves O and the log-sum-exp unchanged mathematically, so the O
-//    rescale (an AGPR round trip) is rare and sits on a wave-uniform branch,
-//    as does the causal / ragged-tail mask;
+//    rescale is rare and sits on a wave-uniform branch, as does the causal /
+//    ragged-tail mask;
 //  * causal: key tiles past the workgroup's last query are never loaded and
 //    sub-tiles past a wave's last query are skipped by that wave;
 //  * heaviest causal query tiles are dispatched first, and consecutive
@@ -59,14 +57,12 @@ struct FwdTile {
   static constexpr int CH = D / 8;              // 16-byte chunks per row
   static constexpr int NC = D / 16;             // 16-deep k-chunks of the QK product
   static constexpr int NDB = D / 32;            // 32-wide head-dim blocks of O
-  static constexpr int NG = D / 16;             // 16-dim groups of the V layout
-  static constexpr int GSTRIDE = BC * 32 + 128; // bytes per V group (64 keys x 32 B + pad)
-  static constexpr int KBYTES = CH * BC * 16;   // K tile bytes: [chunk][key][16 B]
-  static constexpr int VBYTES = NG * GSTRIDE;   // V tile bytes
-  static constexpr int SLOT = KBYTES + VBYTES;  // one ring slot
+  static constexpr int NO = D / 64;             // 64-dim octets (8 chunks, 128 B) per row
+  static constexpr int KT = BC * D * 2;         // bytes of one K (or V) tile: [octet][key][128 B]
+  static constexpr int VREG = NBUF * KT;        // the V ring follows the K ring
   static constexpr int IPW = CH / NW;           // DMA instructions per wave per tensor per tile
-  static_assert(IPW * NW == CH && 2 * NG == CH, "DMA split");
-  static_assert(NBUF * SLOT <= 163840, "LDS budget");
+  static_assert(IPW * NW == CH, "DMA split");
+  static_assert(2 * NBUF * KT <= 163840, "LDS budget");
 };
 
 // O^T += V^T P^T for one 32x32 block. With one query block per wave O^T
@@ -98,6 +94,15 @@ __device__ __forceinline__ void o_fence(f32x16 (&oacc)[QB][NDB]) {
 // reference before the reference is raised and O rescaled.
 constexpr float kRescaleThreshold = 8.f;
 
+// A tile is stored row-major by 64-dim octets: octet o of key k is 128 bytes
+// at o*64*128 + k*128, so one copy instruction moves 8 keys x 128 contiguous
+// bytes. Inside the octet the eight 16-byte chunks are XOR-swizzled per key
+// (K and V differently) so that the fragment reads are free of bank
+// conflicts: 16 keys at one logical chunk (K) and 4 keys x 4 chunks (the
+// transposing V read) land in distinct 16-byte bank groups.
+__device__ __forceinline__ int swz_k(int key) { return (key >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int key) { return 4 * ((key >> 1) & 1); }
+
 template <int D, int QB, bool CAUSAL>
 __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
                                                           uint16_t* __restrict__ O, float* __restrict__ LSE,
                                                           int N, float scale, float c2, int n_qt, int BH) {
   using T = FwdTile<D, QB>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[T::NBUF * T::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::NBUF * T::KT];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform: scalar branches below
@@ -120,24 +125,22 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   const uint16_t* Vh = V + head;
   const int wq0 = q0 + T::WR * w;  // first query row of this wave
 
-  // ---- DMA of one K/V tile into a ring slot; wave w copies K chunks and V
-  // group halves w*IPW .. w*IPW + IPW - 1 ----
+  // ---- DMA of one K/V tile into a ring slot: instruction v of the tile
+  // (wave w issues v = w*IPW .. w*IPW + IPW - 1 for each tensor) copies octet
+  // v / 8 of keys k0 + 8*(v % 8) .. + 7; lane l fetches the logical chunk that
+  // its LDS position holds ----
   auto dma = [&](int j, int slot) __attribute__((always_inline)) {
-    const uint32_t kb = lds_addr(lds) + slot * T::SLOT;
-    const uint32_t vb = kb + T::KBYTES;
-    const int k0 = j * T::BC;
-    const uint16_t* krow = Kh + (size_t)min(k0 + l, N - 1) * D;  // keys past N: any valid row, masked later
+    const uint32_t kb = lds_addr(lds) + slot * T::KT;
+    const uint32_t vb = kb + T::VREG;
 #pragma unroll
     for (int i = 0; i < T::IPW; ++i) {
-      const int c = w * T::IPW + i;  // K: chunk c of keys k0 .. k0 + 63
-      global_load_lds16(krow + 8 * c, kb + c * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < T::IPW; ++i) {
-      const int v = w * T::IPW + i;  // V: group v / 2, keys k0 + 32 * (v % 2) .. + 31
-      const int key = min(k0 + 32 * (v & 1) + (l >> 1), N - 1);
-      global_load_lds16(Vh + (size_t)key * D + 16 * (v >> 1) + 8 * (l & 1),
-                        vb + (v >> 1) * T::GSTRIDE + (v & 1) * 1024);
+      const int v = w * T::IPW + i, o = v >> 3, b = v & 7;
+      const int kr = 8 * b + (l >> 3);  // key within the tile
+      const int key = min(j * T::BC + kr, N - 1);  // keys past N: any valid row, masked later
+      const uint16_t* src = Kh + (size_t)key * D + 64 * o;
+      global_load_lds16(src + 8 * ((l & 7) ^ swz_k(kr)), kb + o * (T::BC * 128) + b * 1024);
+      const uint16_t* vsrc = Vh + (size_t)key * D + 64 * o;
+      global_load_lds16(vsrc + 8 * ((l & 7) ^ swz_v(kr)), vb + o * (T::BC * 128) + b * 1024);
     }
   };
 
@@ -164,13 +167,23 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     }
   }
 
-  // Per-lane LDS byte offsets within a slot. K fragment (A operand): key lq
-  // of the sub-tile, chunk 2c + hf. V^T fragment (transposing read): lane
-  // (g, s) of 16-lane group g addresses key 4*(g/2) + s/4 (+8 for the second
-  // half) and head dims 16*(g%2) + 4*(s%4) (+32 per head-dim block).
+  // Per-lane LDS byte offsets within a ring slot. K fragment (A operand of
+  // S^T): key lq of the sub-tile, logical chunk 2c + hf; the swizzle makes the
+  // offset depend on c % 4 (k_lane[c % 4]), the octet c / 4 is an immediate.
+  // V^T fragment (transposing read): lane (g, s) of 16-lane group g addresses
+  // key 4*(g/2) + s/4 (+8 for the second read) and head dims 16*(g%2) +
+  // 4*(s%4) of 32-dim block db; the offset depends on db % 2 (v_lane[db % 2]),
+  // the octet db / 2 and the key offsets are immediates.
   const int g16 = l >> 4, s16 = l & 15;
-  const int k_lane = hf * 1024 + lq * 16;
-  const int v_lane = T::KBYTES + (g16 & 1) * T::GSTRIDE + (4 * (g16 >> 1) + (s16 >> 2)) * 32 + 8 * (s16 & 3);
+  int k_lane[4], v_lane[2];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) k_lane[c] = lq * 128 + 16 * ((2 * c + hf) ^ swz_k(lq));
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int key = 4 * (g16 >> 1) + (s16 >> 2);
+    const int chunk = 4 * a + 2 * (g16 & 1) + ((s16 & 3) >> 1);
+    v_lane[a] = T::VREG + key * 128 + 16 * (chunk ^ swz_v(key)) + 8 * (s16 & 1);
+  }
 
   f32x16 sA[QB], sB[QB];    // S^T of one 32-key sub-tile per query block (VGPRs)
   f32x16 oacc[QB][T::NDB];  // O^T (AGPRs): lane l owns query l % 32 of each block
@@ -185,11 +198,16 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     lsum[qb] = 0.f;
   }
 
-  // S^T for the 32-key half h of the tile whose K sits at k_addr
-  auto qk = [&](f32x16(&s)[QB], int k_addr, int h) __attribute__((always_inline)) {
+  // K fragment c (A operand of S^T) of 32-key half h of the tile in the ring
+  // slot at byte offset k_slot
+  auto k_frag = [&](int k_slot, int h, int c) __attribute__((always_inline)) {
+    return *(const bf16x8*)(lds + (k_lane[c & 3] + k_slot) + ((c >> 2) * (T::BC * 128) + h * 32 * 128));
+  };
+  // S^T for the 32-key half h of the tile in the slot at k_slot
+  auto qk = [&](f32x16(&s)[QB], int k_slot, int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
-      const bf16x8 a = *(const bf16x8*)(lds + k_addr + (c * 2048 + h * 512));
+      const bf16x8 a = k_frag(k_slot, h, c);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qop[qb][c], c == 0 ? (f32x16){} : s[qb]);
     }
@@ -250,9 +268,6 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     const float p1 = fast_exp2(fmaf(s[qb][r + 1], c2, -mc[qb]));
     ps[qb] += p0 + p1;
     const bf16x2 two = to_bf16x2(p0, p1);
-    // pins the pair's arithmetic before the next scheduling fence (pure
-    // arithmetic would otherwise sink next to its use in the P V MFMAs)
-    asm volatile("" ::"v"(two), "v"(ps[qb]));
     pb[qb][r >> 3][r & 7] = two[0];
     pb[qb][r >> 3][(r & 7) + 1] = two[1];
   };
@@ -260,34 +275,32 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   constexpr int NPAIR = 8 * QB;
   auto pair_qb = [](int i) { return (i >> 2) % QB; };
   auto pair_r = [](int i) { return 8 * (i / (4 * QB)) + 2 * (i & 3); };
-  // K fragments (A operand of S^T) of 32-key half h of the tile at k_addr
-  auto load_k = [&](bf16x8(&kf)[T::NC], int k_addr, int h) __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) kf[c] = *(const bf16x8*)(lds + k_addr + (c * 2048 + h * 512));
-  };
   // V^T fragment (A operand of O^T) for 16-key chunk kc and head-dim block db
-  // of 32-key half h of the tile at v_addr
-  auto load_v = [&](int v_addr, int h, int kc, int db) __attribute__((always_inline)) {
-    const uint8_t* src = lds + v_addr + (db * 2 * T::GSTRIDE + (32 * h + 16 * kc) * 32);
-    const s16x4 lo = lds_read_tr16(src);
-    const s16x4 hi = lds_read_tr16(src + 8 * 32);
+  // of 32-key half h of the tile in the slot at v_slot
+  auto load_v = [&](int v_slot, int h, int kc, int db) __attribute__((always_inline)) {
+    const int imm = (db >> 1) * (T::BC * 128) + (32 * h + 16 * kc) * 128;
+    const s16x4 lo = lds_read_tr16(lds + (v_lane[db & 1] + v_slot) + imm);
+    const s16x4 hi = lds_read_tr16(lds + (v_lane[db & 1] + v_slot) + (imm + 8 * 128));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  bf16x8 kf[T::NC];  // K fragments of the next sub-tile to score (loaded one step ahead)
+  bf16x8 kf[T::NC];  // K fragments of the next sub-tile to score
 
-  // One pipeline step: finish sub-tile t (its V at v_addr, half t % 2), score
-  // sub-tile t + 1 (its K already in kf; needs t + 1 < n_st) and fetch the K
-  // fragments of sub-tile t + 2 (half t % 2 of the tile at kp_addr). The
-  // instruction order is pinned by scheduling fences so that the matrix core
-  // has work queued at every point: first the score MFMAs of t + 1, each
-  // k-chunk followed by some probabilities of t and one V^T fragment read;
-  // then the P V MFMAs of t, each head-dim block followed by the last
-  // probabilities (first half), a slice of the row maximum of t + 1 and part
-  // of the next K fragments.
-  auto step_body = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+  // One pipeline step: finish sub-tile t (its V in the slot at v_slot, half
+  // t % 2), score sub-tile t + 1 (needs t + 1 < n_st; its first two K
+  // fragments are already in kf, the others are read two k-chunks ahead) and
+  // fetch the first K fragments of sub-tile t + 2 (half t % 2 of the slot at
+  // kp_slot). The source order is the intended issue order, so that the
+  // matrix core has independent work at every point: the score MFMAs of t + 1
+  // with most probabilities of t and the first V^T reads between them, then
+  // the P V MFMAs of t with the last probabilities and V^T reads, the row
+  // maximum of t + 1 and the next K fragments. With two waves per SIMD the
+  // hardware interleaves the waves; pinning the order further with
+  // scheduling fences measured no better.
+  auto step_body = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
     const int h = t & 1;
+    const int kp_slot_cur = h ? kp_slot : v_slot;  // slot of sub-tile t + 1 (rest of its K fragments)
     bf16x8 vf[2][T::NDB], pb[QB][2];
     float ps[QB], mc[QB], mx[QB];
 #pragma unroll
@@ -301,11 +314,11 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) nxt[qb] = mfma32x32x16(kf[c], qop[qb][c], c == 0 ? (f32x16){} : nxt[qb]);
+      if (c + 2 < T::NC) kf[c + 2] = k_frag(kp_slot_cur, (t + 1) & 1, c + 2);
 #pragma unroll
       for (int i = EARLY * c / T::NC; i < EARLY * (c + 1) / T::NC; ++i)
         prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
-      vf[c / T::NDB][c % T::NDB] = load_v(v_addr, h, c / T::NDB, c % T::NDB);
-      __builtin_amdgcn_sched_barrier(0);
+      if (c < T::NDB) vf[0][c] = load_v(v_slot, h, 0, c);  // the 16-key chunk kc = 1 follows below
     }
     constexpr int PER = 16 / (2 * T::NDB);  // max elements per query block per head-dim block
 #pragma unroll
@@ -317,15 +330,13 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
 #pragma unroll
         for (int p = EARLY + (NPAIR - EARLY) * i / T::NDB; p < EARLY + (NPAIR - EARLY) * (i + 1) / T::NDB; ++p)
           prob_pair(cur, pb, ps, mc, pair_qb(p), pair_r(p));
+        vf[1][i] = load_v(v_slot, h, 1, i);
       }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int e = 0; e < PER; ++e) mx[qb] = fmaxf(mx[qb], nxt[qb][i * PER + e]);
-#pragma unroll
-      for (int c = i * T::NC / (2 * T::NDB); c < (i + 1) * T::NC / (2 * T::NDB); ++c)
-        kf[c] = *(const bf16x8*)(lds + kp_addr + (c * 2048 + h * 512));
-      __builtin_amdgcn_sched_barrier(0);
+      if (i >= 2 * T::NDB - 2) kf[i - (2 * T::NDB - 2)] = k_frag(kp_slot, h, i - (2 * T::NDB - 2));
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -334,14 +345,14 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     }
   };
   // the same when sub-tile t + 1 is known to be fully visible
-  auto clean_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+  auto clean_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                         __attribute__((always_inline)) {
-    step_body(cur, nxt, t, v_addr, kp_addr);
+    step_body(cur, nxt, t, v_slot, kp_slot);
     maybe_rescale();
   };
-  auto full_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+  auto full_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
-    step_body(cur, nxt, t, v_addr, kp_addr);
+    step_body(cur, nxt, t, v_slot, kp_slot);
     if (needs_mask(t + 1)) {
       mask(nxt, t + 1);
       tile_max(nxt);
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     maybe_rescale();
   };
   // the wave's last sub-tile: probabilities and P V only
-  auto last_step = [&](f32x16(&cur)[QB], int t, int v_addr) __attribute__((always_inline)) {
+  auto last_step = [&](f32x16(&cur)[QB], int t, int v_slot) __attribute__((always_inline)) {
     bf16x8 pb[QB][2];
     float ps[QB], mc[QB];
 #pragma unroll
@@ -363,19 +374,19 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < T::NDB; ++db) {
-        const bf16x8 a = load_v(v_addr, t & 1, kc, db);
+        const bf16x8 a = load_v(v_slot, t & 1, kc, db);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], a, pb[qb][kc]);
       }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
   };
-  auto tail_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_addr, int kp_addr)
+  auto tail_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
     if (t + 1 < n_st)
-      full_step(cur, nxt, t, v_addr, kp_addr);
+      full_step(cur, nxt, t, v_slot, kp_slot);
     else if (t < n_st)
-      last_step(cur, t, v_addr);
+      last_step(cur, t, v_slot);
   };
   // End of tile j: tile j + 2 resident for every wave (its K is fetched from
   // the next step on) and every wave done with tile j, whose ring slot then
@@ -395,12 +406,13 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   if (n_kt > 2) dma(2, 2);
   if (n_kt > 3) dma(3, 3);
   if (n_st > 0) {
-    qk(sA, k_lane, 0);
+    qk(sA, 0, 0);
     if (needs_mask(0)) mask(sA, 0);
     tile_max(sA);
     maybe_rescale();
   }
-  load_k(kf, k_lane, 1);  // sub-tile 1 (tile 0, second half)
+  kf[0] = k_frag(0, 1, 0);  // sub-tile 1 (tile 0, second half)
+  kf[1] = k_frag(0, 1, 1);
   // Leading sub-tiles that need no mask: the steady-state loop runs the tiles
   // whose both steps start such a sub-tile, with no branch but the rare
   // rescale; the remaining tiles (diagonal, ragged end, or waves that are
@@ -411,15 +423,15 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   const int j_clean = max(0, (n_clean - 1) / 2);
   int j = 0;
   for (; j < j_clean; ++j) {
-    const int s0 = (j & 3) * T::SLOT, s1 = ((j + 1) & 3) * T::SLOT;
-    clean_step(sA, sB, 2 * j, s0 + v_lane, s1 + k_lane);
-    clean_step(sB, sA, 2 * j + 1, s0 + v_lane, s1 + k_lane);
+    const int s0 = (j & 3) * T::KT, s1 = ((j + 1) & 3) * T::KT;
+    clean_step(sA, sB, 2 * j, s0, s1);
+    clean_step(sB, sA, 2 * j + 1, s0, s1);
     end_tile(j);
   }
   for (; j < n_kt; ++j) {
-    const int s0 = (j & 3) * T::SLOT, s1 = ((j + 1) & 3) * T::SLOT;
-    tail_step(sA, sB, 2 * j, s0 + v_lane, s1 + k_lane);
-    tail_step(sB, sA, 2 * j + 1, s0 + v_lane, s1 + k_lane);
+    const int s0 = (j & 3) * T::KT, s1 = ((j + 1) & 3) * T::KT;
+    tail_step(sA, sB, 2 * j, s0, s1);
+    tail_step(sB, sA, 2 * j + 1, s0, s1);
     end_tile(j);
   }
 
