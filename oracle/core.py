@@ -29,6 +29,16 @@ What it computes, and where that is defined:
   each chunk yielding (max, sum, unnormalised output), and the chunks merged
   with the same max-and-sum rule.
 * ``decode`` is the plain definition for one query row per head.
+* ``attention_grad`` is the gradient of the plain definition with respect to
+  Q, K and V for an upstream gradient dO, written out from the chain rule
+  (dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)), dQ = scale dS K,
+  dK = scale dS^T Q), with P materialised. The pages do not print it: they
+  say the backward pass recomputes the score tiles from Q, K and V instead of
+  storing P ("Describe Flash Attention at a high level", section "The two
+  ideas", item 3; "How FlashAttention Speeds Up the Attention Layer", the
+  paragraph on training), and that gradients match standard attention (the
+  first page, "Follow-up questions to expect"). It is pinned by central
+  finite differences of ``attention`` and by closed forms.
 
 Readings where the pages are silent (also listed in the design notes):
   - scale is a caller argument; the pages write 1/sqrt(d); the oracle rounds
@@ -173,6 +183,44 @@ def split_decode(q, kc, vc, nsplit: int, scale: float | None = None):
     L = sum(wi * l_s for wi, (_, l_s, _) in zip(w, parts))
     o = sum(wi * o_s for wi, (_, _, o_s) in zip(w, parts)) / L
     return o, M + np.log(L)
+
+
+def _head_attention_grad(q, k, v, do, causal: bool, s: float):
+    """Gradients of O = softmax(s Q K^T [+ mask]) V for one head, given dO = dL/dO.
+
+    q: [N,d]; k, v: [Nk,d]; do: [N,dv]. Returns (dQ, dK, dV).
+    """
+    _, _, P = _head_attention(q, k, v, causal, s)
+    dV = P.T @ do                                          # O = P V
+    dP = do @ v.T
+    D = np.sum(dP * P, axis=1, keepdims=True)               # rowsum(dP * P) = rowsum(dO * O)
+    dS = P * (dP - D)                                       # softmax Jacobian applied row by row
+    dQ = s * (dS @ k)                                       # S = s Q K^T
+    dK = s * (dS.T @ q)
+    return dQ, dK, dV
+
+
+def attention_grad(q, k, v, do, causal: bool, scale: float, heads=None):
+    """Exact gradients of attention w.r.t. Q, K, V (float64), one head at a time.
+
+    q, k, v, do: [B, H, N, d]. Returns (dQ, dK, dV) with the shapes of q, k,
+    v; heads outside ``heads`` are left as NaN.
+    """
+    q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+    B, H = q.shape[:2]
+    dQ, dK, dV = np.full(q.shape, np.nan), np.full(k.shape, np.nan), np.full(v.shape, np.nan)
+    s = _f32(scale)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        dQ[b, h], dK[b, h], dV[b, h] = _head_attention_grad(q[b, h], k[b, h], v[b, h], do[b, h], causal, s)
+    return dQ, dK, dV
+
+
+def attention_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Backward FLOPs of the recompute method: 10*d per visible (query, key) pair
+    (S recomputed, then dP, dV, dQ and dK, each 2*d)."""
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 10 * d * B * H * pairs
 
 
 def naive_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:
