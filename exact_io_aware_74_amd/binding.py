@@ -26,6 +26,8 @@ SIGNATURES = {
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
+    "fa_bwd_workspace_bytes": (_S, [_I, _I, _I]),
     "fa_naive_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "fa_naive_workspace_bytes": (_S, [_I, _I, _I]),
     "fa_status_str": (ctypes.c_char_p, [_I]),
@@ -138,6 +140,43 @@ def decode(q, kcache, vcache, nsplit: int = 64, out=None):
         st = lib.fa_decode(_ptr(q3), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d, int(nsplit), _stream(q))
     _check("fa_decode", st)
     return o
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, H, N))
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None, out=None, workspace=None):
+    """Gradients (dq, dk, dv) of fwd(q, k, v, causal, scale) for the upstream gradient dout.
+
+    q, k, v, o, dout: [B,H,N,d] bfloat16; lse: the float32 [B,H,N] that fwd
+    returned. ``out`` may pass preallocated (dq, dk, dv); ``workspace`` a
+    device buffer of at least bwd_workspace_bytes(B, H, N) bytes.
+    """
+    lib = load()
+    _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("bwd takes bfloat16 tensors")
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be the contiguous float32 [B, H, N] tensor fwd returned")
+    scale = default_scale(d) if scale is None else float(scale)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3)) if out is None else out
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    need = bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, H, N, d, int(bool(causal)), scale, _ptr(workspace),
+                        workspace.numel() * workspace.element_size(), _stream(q))
+    _check("fa_bwd", st)
+    return dq, dk, dv
 
 
 def naive_workspace_bytes(B: int, H: int, N: int) -> int:

@@ -1,0 +1,420 @@
+// Attention backward with recompute, bf16 in/out, fp32 accumulation, gfx950.
+//
+// The backward pass does not read a stored probability matrix: it recomputes
+// the score tiles from Q, K and V and the forward's per-row log-sum-exp, as
+// "Describe Flash Attention at a high level" (mantramindai.in), section "The
+// two ideas", item 3, and "How FlashAttention Speeds Up the Attention Layer"
+// (hassanahmed.net), the paragraph on training, describe. The gradients are
+// the chain rule of the plain definition (the pages only state that they match
+// standard attention):
+//   P = exp(scale Q K^T - LSE)        (masked entries 0)
+//   dV = P^T dO,   dP = dO V^T,   D = rowsum(dO * O),   dS = P * (dP - D),
+//   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Three kernels:
+//  * bwd_prep: D (fp32) and LSE * log2(e) per query row, into the caller's
+//    workspace (rows padded to a multiple of 64 with zeros);
+//  * bwd_dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys). A
+//    wave keeps its keys' K and V rows in VGPRs as MFMA B operands and streams
+//    64-row Q / dO tiles through LDS. Per 32 queries it recomputes
+//    S = Q K^T and dP = dO V^T (lane l holds key l % 32 and 16 queries), forms
+//    P and dS in registers and accumulates dV += P^T dO and dK += dS^T Q, the
+//    P^T / dS^T operands coming straight from those registers and dO / Q
+//    through the transposing LDS read;
+//  * bwd_dq: one workgroup per 256 queries (8 waves x 32 rows), laid out like
+//    the forward: S^T = K Q^T and dP^T = V dO^T with Q / dO in VGPRs, then
+//    dQ^T += K^T dS^T with K^T from the transposing read. No atomics: dQ is
+//    owned by one wave, so results are deterministic.
+// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into two slots
+// (one barrier per tile), row-major by 64-dim octets with the 16-byte chunks
+// XOR-swizzled per row by one function that keeps both the row-fragment reads
+// (16 rows, one chunk) and the transposing reads (4 rows x 4 chunks) free of
+// bank conflicts.
+#include <float.h>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int BT = 64;  // rows per LDS tile
+
+__device__ __forceinline__ int bswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
+
+template <int D>
+struct BwdTile {
+  static constexpr int NC = D / 16;             // 16-deep k-chunks over the head dim
+  static constexpr int NDB = D / 32;            // 32-wide head-dim blocks
+  static constexpr int BYTES = BT * D * 2;      // one tile
+  static constexpr int NCOPY = BYTES / 1024;    // copy instructions per tile
+};
+
+// Copy instruction v of the tile holding rows r0 .. r0 + 63 of a [rows, D]
+// bf16 matrix: octet v / 8 of rows r0 + 8*(v % 8) .. + 7. Rows past the end
+// repeat the last row (masked by the caller).
+template <int D>
+__device__ __forceinline__ void copy_part(const uint16_t* base, int r0, int rows, uint32_t dst, int v, int l) {
+  const int o = v >> 3, b = v & 7;
+  const int rr = 8 * b + (l >> 3);
+  const int row = min(r0 + rr, rows - 1);
+  global_load_lds16(base + (size_t)row * D + 64 * o + 8 * ((l & 7) ^ bswz(rr)), dst + o * (BT * 128) + b * 1024);
+}
+
+// Per-lane byte offsets into a tile. Row fragment (MFMA A or B operand taken
+// along a row): row 32*h + lq, logical chunk 2c + hf -> row_lane[c % 4] +
+// (c / 4) * 8192 + h * 4096. Transposing read for 16-row chunk kc and 32-col
+// block db: lane (g, s) addresses row 4*(g/2) + s/4 (+8 for the second read)
+// and cols 16*(g%2) + 4*(s%4) -> tr_lane[db % 2][second] + (db / 2) * 8192 +
+// (32*h + 16*kc) * 128.
+struct TileLanes {
+  int row[4];
+  int tr[2][2];
+  __device__ __forceinline__ explicit TileLanes(int l) {
+    const int hf = l >> 5, lq = l & 31, g = l >> 4, s = l & 15;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) row[c] = lq * 128 + 16 * ((2 * c + hf) ^ bswz(lq));
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = 4 * (g >> 1) + (s >> 2) + 8 * hi;
+        const int chunk = 4 * a + 2 * (g & 1) + ((s & 3) >> 1);
+        tr[a][hi] = r * 128 + 16 * (chunk ^ bswz(r)) + 8 * (s & 1);
+      }
+  }
+};
+
+__device__ __forceinline__ bf16x8 row_frag(const uint8_t* lds, int tile, const TileLanes& tl, int h, int c) {
+  return *(const bf16x8*)(lds + (tile + tl.row[c & 3]) + ((c >> 2) * (BT * 128) + h * 32 * 128));
+}
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t* lds, int tile, const TileLanes& tl, int h, int kc, int db) {
+  const int imm = (db >> 1) * (BT * 128) + (32 * h + 16 * kc) * 128;
+  const s16x4 lo = lds_read_tr16(lds + (tile + tl.tr[db & 1][0]) + imm);
+  const s16x4 hi = lds_read_tr16(lds + (tile + tl.tr[db & 1][1]) + imm);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// ---- D = rowsum(dO * O) and LSE in exp2 units, per query row ----
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ LSE, float* __restrict__ lse2,
+                                                       float* __restrict__ Dsum, int BH, int N, int Npad) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int prow = gid / LPR, part = gid % LPR;  // padded row index over BH * Npad
+  const int bh = prow / Npad, i = prow % Npad;
+  const bool valid = bh < BH && i < N;
+  float acc = 0.f;
+  if (valid) {
+    const size_t off = ((size_t)bh * N + i) * D + 8 * part;
+    const u32x4 a = *(const u32x4*)(O + off), b = *(const u32x4*)(dO + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (part == 0 && bh < BH) {
+    lse2[prow] = valid ? LSE[(size_t)bh * N + i] * kLog2e : 0.f;
+    Dsum[prow] = valid ? acc : 0.f;
+  }
+}
+
+// ---- dK, dV: one workgroup per 128 keys of one head ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                          const float* __restrict__ lse2, const float* __restrict__ Dsum,
+                                                          uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+                                                          int Npad, float scale, float c2, int BH) {
+  using T = BwdTile<D>;
+  constexpr int SLOT = 2 * T::BYTES + 512;  // Q tile, dO tile, 64 x (LSE2, D) floats
+  constexpr int IPW = 2 * T::NCOPY / 4;     // copy instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, hf = l >> 5, lq = l & 31;
+  const int bh = blockIdx.x % BH, kt = blockIdx.x / BH;  // key tiles of a head in order: heaviest first
+  const int k0 = kt * 128, kw0 = k0 + 32 * w;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t *Qh = Q + head, *Kh = K + head, *Vh = V + head, *dOh = dO + head;
+  const float* L2h = lse2 + (size_t)bh * Npad;
+  const float* Dh = Dsum + (size_t)bh * Npad;
+
+  // K and V rows of this wave's keys as B operands: lane (key kw0 + lq, half
+  // hf) holds head dims 16c + 8hf .. + 7
+  bf16x8 kT[T::NC], vT[T::NC];
+  {
+    const int key = kw0 + lq;
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+      if (key < N) {
+        kT[c] = *(const bf16x8*)(Kh + (size_t)key * D + 16 * c + 8 * hf);
+        vT[c] = *(const bf16x8*)(Vh + (size_t)key * D + 16 * c + 8 * hf);
+      } else {
+        kT[c] = (bf16x8){};
+        vT[c] = (bf16x8){};
+      }
+    }
+  }
+  f32x16 dv[T::NDB], dk[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) {
+    dv[db] = (f32x16){};
+    dk[db] = (f32x16){};
+  }
+
+  const TileLanes tl(l);
+  const int n_qt = (N + BT - 1) / BT;
+  const int qt0 = CAUSAL ? k0 / BT : 0;  // earlier query tiles see none of these keys
+  auto copy = [&](int qt, int slot) __attribute__((always_inline)) {
+    const uint32_t base = lds_addr(lds) + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int v = w * IPW + i;  // 0 .. NCOPY - 1: Q, then dO
+      if (v < T::NCOPY)
+        copy_part<D>(Qh, qt * BT, N, base, v, l);
+      else
+        copy_part<D>(dOh, qt * BT, N, base + T::BYTES, v - T::NCOPY, l);
+    }
+    if (w == 0 && l < 32) {  // LSE2 then D of the tile's 64 rows (the workspace is padded)
+      const float* src = (l < 16 ? L2h : Dh) + qt * BT + 4 * (l & 15);
+      global_load_lds16(src, base + 2 * T::BYTES);
+    }
+  };
+
+  if (qt0 < n_qt) copy(qt0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int qt = qt0; qt < n_qt; ++qt) {
+    const int slot = (qt - qt0) & 1;
+    if (qt + 1 < n_qt) copy(qt + 1, slot ^ 1);
+    const int tQ = slot * SLOT, tdO = tQ + T::BYTES;
+    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int qb0 = qt * BT + 32 * h;  // first query of the 32-row block
+      if (qb0 >= N || (CAUSAL && qb0 + 31 < kw0)) continue;
+      f32x16 sc = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c) {
+        sc = mfma32x32x16(row_frag(lds, tQ, tl, h, c), kT[c], sc);
+        dp = mfma32x32x16(row_frag(lds, tdO, tl, h, c), vT[c], dp);
+      }
+      // lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf
+      const bool need_mask = (qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31);
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 L4 = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
+        const f32x4 D4 = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int r = 4 * rb + e;
+          float p0 = fast_exp2(fmaf(sc[r], c2, -L4[e]));
+          float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L4[e + 1]));
+          if (need_mask) {
+            const int q = qb0 + 8 * rb + 4 * hf + e, key = kw0 + lq;
+            p0 = (q < N && (!CAUSAL || key <= q)) ? p0 : 0.f;
+            p1 = (q + 1 < N && (!CAUSAL || key <= q + 1)) ? p1 : 0.f;
+          }
+          const float d0 = p0 * (dp[r] - D4[e]), d1 = p1 * (dp[r + 1] - D4[e + 1]);
+          const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
+          pb[r >> 3][r & 7] = pp[0];
+          pb[r >> 3][(r & 7) + 1] = pp[1];
+          sb[r >> 3][r & 7] = ss[0];
+          sb[r >> 3][(r & 7) + 1] = ss[1];
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
+      // the lane's queries), B = dO / Q through the transposing read
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+          dv[db] = mfma32x32x16(pb[kc], tr_frag(lds, tdO, tl, h, kc, db), dv[db]);
+          dk[db] = mfma32x32x16(sb[kc], tr_frag(lds, tQ, tl, h, kc, db), dk[db]);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // tile qt + 1 resident; every wave done with tile qt
+  }
+
+  // lane l holds head dim 32*db + lq of keys kw0 + (r%4) + 8(r/4) + 4hf
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw0 + (r & 3) + 8 * (r >> 2) + 4 * hf;
+      if (key < N) {
+        const size_t off = head + (size_t)key * D + 32 * db + lq;
+        dV[off] = to_bf16_bits(dv[db][r]);
+        dK[off] = to_bf16_bits(dk[db][r] * scale);
+      }
+    }
+}
+
+// ---- dQ: one workgroup per 256 queries of one head ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                        const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                                                        const float* __restrict__ lse2, const float* __restrict__ Dsum,
+                                                        uint16_t* __restrict__ dQ, int N, int Npad, float scale, float c2,
+                                                        int n_qt, int BH) {
+  using T = BwdTile<D>;
+  constexpr int SLOT = 2 * T::BYTES;      // K tile, V tile
+  constexpr int IPW = 2 * T::NCOPY / 8;   // copy instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, hf = l >> 5, lq = l & 31;
+  const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
+  const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;  // heaviest causal query tiles first
+  const int q0 = qt * 256, wq0 = q0 + 32 * w;
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t *Qh = Q + head, *Kh = K + head, *Vh = V + head, *dOh = dO + head;
+
+  // Q and dO rows as B operands: lane (query wq0 + lq, half hf), dims 16c + 8hf .. + 7
+  const int qrow = wq0 + lq;
+  bf16x8 qT[T::NC], doT[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    if (qrow < N) {
+      qT[c] = *(const bf16x8*)(Qh + (size_t)qrow * D + 16 * c + 8 * hf);
+      doT[c] = *(const bf16x8*)(dOh + (size_t)qrow * D + 16 * c + 8 * hf);
+    } else {
+      qT[c] = (bf16x8){};
+      doT[c] = (bf16x8){};
+    }
+  }
+  const float lq2 = qrow < N ? lse2[(size_t)bh * Npad + qrow] : 0.f;
+  const float dq_d = qrow < N ? Dsum[(size_t)bh * Npad + qrow] : 0.f;
+  f32x16 dqT[T::NDB];
+#pragma unroll
+  for (int db = 0; db < T::NDB; ++db) dqT[db] = (f32x16){};
+
+  const TileLanes tl(l);
+  const int kv_end = CAUSAL ? min(N, q0 + 256) : N;
+  const int n_kt = (kv_end + BT - 1) / BT;
+  const int wv_end = CAUSAL ? min(N, wq0 + 32) : N;
+  const int n_st = wq0 < N ? (wv_end + 31) / 32 : 0;  // 32-key sub-tiles this wave needs
+  auto copy = [&](int j, int slot) __attribute__((always_inline)) {
+    const uint32_t base = lds_addr(lds) + slot * SLOT;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int v = w * IPW + i;
+      if (v < T::NCOPY)
+        copy_part<D>(Kh, j * BT, N, base, v, l);
+      else
+        copy_part<D>(Vh, j * BT, N, base + T::BYTES, v - T::NCOPY, l);
+    }
+  };
+
+  if (n_kt > 0) copy(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int j = 0; j < n_kt; ++j) {
+    const int slot = j & 1;
+    if (j + 1 < n_kt) copy(j + 1, slot ^ 1);
+    const int tK = slot * SLOT, tV = tK + T::BYTES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 2 * j + h;
+      if (t >= n_st) continue;
+      f32x16 sT = (f32x16){}, dpT = (f32x16){};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c) {
+        sT = mfma32x32x16(row_frag(lds, tK, tl, h, c), qT[c], sT);
+        dpT = mfma32x32x16(row_frag(lds, tV, tl, h, c), doT[c], dpT);
+      }
+      // lane: query qrow; element r: key 32t + (r%4) + 8(r/4) + 4hf
+      const bool need_mask = (32 * t + 32 > N) || (CAUSAL && 32 * t + 31 > wq0);
+      bf16x8 sb[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = fast_exp2(fmaf(sT[r], c2, -lq2));
+        float p1 = fast_exp2(fmaf(sT[r + 1], c2, -lq2));
+        if (need_mask) {
+          const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
+          p0 = (key < N && (!CAUSAL || key <= qrow)) ? p0 : 0.f;
+          p1 = (key + 1 < N && (!CAUSAL || key + 1 <= qrow)) ? p1 : 0.f;
+        }
+        const bf16x2 ss = to_bf16x2(p0 * (dpT[r] - dq_d), p1 * (dpT[r + 1] - dq_d));
+        sb[r >> 3][r & 7] = ss[0];
+        sb[r >> 3][(r & 7) + 1] = ss[1];
+      }
+      // dQ^T += K^T dS^T: A = K^T (transposing read), B = dS^T from the registers
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) dqT[db] = mfma32x32x16(tr_frag(lds, tK, tl, h, kc, db), sb[kc], dqT[db]);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+
+  // lane l holds query qrow, head dims 32*db + (r%4) + 8(r/4) + 4hf
+  if (qrow < N) {
+    uint16_t* out = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x2 a = to_bf16x2(dqT[db][4 * rb] * scale, dqT[db][4 * rb + 1] * scale);
+        const bf16x2 b = to_bf16x2(dqT[db][4 * rb + 2] * scale, dqT[db][4 * rb + 3] * scale);
+        *(bf16x4*)(out + 32 * db + 8 * rb + 4 * hf) = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                        void* dq, void* dk, void* dv, float* ws, int B, int H, int N, float scale, hipStream_t s) {
+  const int BH = B * H;
+  int Npad = bwd_rows_padded(N);
+  float* lse2 = ws;
+  float* dsum = ws + (size_t)BH * Npad;
+  float c2 = scale * kLog2e;  // a positive floor keeps masked scores at 0 when scale is 0
+  if (!(c2 >= FLT_MIN)) c2 = FLT_MIN;
+  const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v,
+                 *op = (const uint16_t*)o, *dop = (const uint16_t*)dout;
+  uint16_t *dqp = (uint16_t*)dq, *dkp = (uint16_t*)dk, *dvp = (uint16_t*)dv;
+
+  const long long prep_threads = (long long)BH * Npad * (D / 8);
+  dim3 g0((unsigned)((prep_threads + 255) / 256)), b0(256);
+  void* a0[] = {&op, &dop, (void*)&lse, &lse2, &dsum, (void*)&BH, &N, &Npad};
+  hipError_t e = hipLaunchKernel((const void*)&bwd_prep_kernel<D>, g0, b0, a0, 0, s);
+  if (e != hipSuccess) return e;
+
+  dim3 g1((unsigned)(((N + 127) / 128) * BH)), b1(256);
+  void* a1[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dkp, &dvp, &N, &Npad, &scale, &c2, (void*)&BH};
+  e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<D, CAUSAL>, g1, b1, a1, 0, s);
+  if (e != hipSuccess) return e;
+
+  int n_qt = (N + 255) / 256;
+  dim3 g2((unsigned)(n_qt * BH)), b2(512);
+  void* a2[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dqp, &N, &Npad, &scale, &c2, &n_qt, (void*)&BH};
+  return hipLaunchKernel((const void*)&bwd_dq_kernel<D, CAUSAL>, g2, b2, a2, 0, s);
+}
+
+}  // namespace
+
+int bwd_rows_padded(int N) { return (N + BT - 1) / BT * BT; }
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d, bool causal, float scale,
+                      hipStream_t s) {
+  if (d == 64)
+    return causal ? launch_bwd_t<64, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s)
+                  : launch_bwd_t<64, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s);
+  return causal ? launch_bwd_t<128, true>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s)
+                : launch_bwd_t<128, false>(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, scale, s);
+}
+
+}  // namespace fa

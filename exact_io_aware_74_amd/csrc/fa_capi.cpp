@@ -136,6 +136,39 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o, in
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return 2 * (size_t)B * (size_t)H * (size_t)fa::bwd_rows_padded(N) * sizeof(float);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  const int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 2);
+  if (st != FA_OK) return st == 1 ? FA_OK : st;
+  if (!dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N);
+  if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  const size_t bytes = (size_t)B * H * (size_t)N * (size_t)d * 2, lbytes = (size_t)B * H * (size_t)N * 4;
+  const void* ins[] = {q, k, v, o, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* out : outs) {
+    for (const void* in : ins)
+      if (overlaps(out, bytes, in, bytes)) return FA_ERR_INVALID_ARG;
+    if (overlaps(out, bytes, lse, lbytes) || overlaps(out, bytes, workspace, need)) return FA_ERR_INVALID_ARG;
+  }
+  if (overlaps(dq, bytes, dk, bytes) || overlaps(dq, bytes, dv, bytes) || overlaps(dk, bytes, dv, bytes))
+    return FA_ERR_INVALID_ARG;
+  for (const void* in : ins)
+    if (overlaps(workspace, need, in, bytes)) return FA_ERR_INVALID_ARG;
+  if (overlaps(workspace, need, lse, lbytes)) return FA_ERR_INVALID_ARG;
+  const hipError_t e = fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal != 0,
+                                      scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 size_t fa_naive_workspace_bytes(int B, int H, int N) {
   if (B < 0 || H < 0 || N < 0) return 0;
   const unsigned __int128 b = (unsigned __int128)B * H * N * N * 4u;

@@ -17,6 +17,13 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* ws,
                          int B, int H, int Lkv, int d, int nsplit, int chunk, hipStream_t s);
 
+// Backward with recompute: dq, dk, dv from q, k, v, o, dout and the forward's
+// lse. `ws` holds 2 * B*H*bwd_rows_padded(N) floats.
+int bwd_rows_padded(int N);
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* ws, int B, int H, int N, int d, bool causal, float scale,
+                      hipStream_t s);
+
 // Naive three-kernel ablation; `S` holds B*H*N*N floats.
 hipError_t launch_naive(const void* q, const void* k, const void* v, void* o, float* lse, float* S,
                         int B, int H, int N, int d, bool causal, float scale, hipStream_t s);

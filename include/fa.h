@@ -105,6 +105,35 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o,
 size_t fa_decode_workspace_bytes(int B, int H, int Lkv, int d, int nsplit);
 
 /*
+ * fa_bwd -- gradients of fa_fwd with respect to Q, K and V, computed with the
+ * recompute method: the score tiles are rebuilt from Q, K and the forward's
+ * LSE instead of being stored. Sources: mantramindai.in, section "The two
+ * ideas", item 3 (recompute in backward); hassanahmed.net, the paragraph on
+ * training. The gradient is the chain rule of the definition (P = softmax of
+ * the scaled, masked logits): dV = P^T dO; dS = P * (dO V^T - rowsum(dO * O));
+ * dQ = scale dS K; dK = scale dS^T Q.
+ *
+ *   q, k, v, o  const bf16 [B,H,N,d]: the forward's inputs and output
+ *   dout        const bf16 [B,H,N,d]: dL/dO
+ *   lse         const float32 [B,H,N]: the LSE fa_fwd wrote for the same call
+ *   dq, dk, dv  bf16 [B,H,N,d] outputs; may not alias any input or each other
+ *   B, H, N, d, causal, scale: as passed to fa_fwd
+ *   workspace   caller-owned device buffer of at least
+ *               fa_bwd_workspace_bytes(B,H,N) bytes (float32 row statistics;
+ *               contents on entry are ignored), 16-byte aligned
+ * Arithmetic: bf16 MFMA products, fp32 accumulation; P and dS are rounded to
+ * bf16 (nearest even) as MFMA operands; dq, dk, dv are rounded once to bf16.
+ * The result is deterministic (no atomics). Errors as fa_fwd; a workspace that
+ * is NULL, misaligned or too small gives FA_ERR_INVALID_ARG.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of backward workspace: 2 * B*H*ceil(N/64)*64 * 4 (0 on bad sizes). */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
  * fa_naive_fwd -- the three-step attention of the pages, kept as an ablation:
  * kernel 1 writes S = scale * Q K^T (masked entries -inf) to `workspace` as
  * float32 [B,H,N,N]; kernel 2 turns each row into softmax probabilities in

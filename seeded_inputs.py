@@ -153,3 +153,10 @@ def random_case(seed: int, B: int, H: int, N: int, d: int, dtype: str, nk: int |
         x = (rng.standard_normal((B, H, rows, d), dtype=np.float32) * np.float32(sd)).astype(np.float32)
         outs.append(f32_to_bf16_bits(x) if dtype == "bf16" else x)
     return tuple(outs)
+
+
+def upstream_grad(seed: int, B: int, H: int, N: int, d: int, dtype: str) -> np.ndarray:
+    """Seeded upstream gradient dL/dO for backward tests: N(0,1), [B,H,N,d], cast like the inputs."""
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 5000 + seed, B, H, N, d]))
+    x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
-              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes"):
+              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes"):
         assert n in names
     assert len(names) == len(set(names))
 
@@ -148,3 +148,36 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
     assert "oracle" not in open(HEADER).read().lower()
+
+
+def bwd(lib, *, q=A, k=Bp, v=C, o=Dp, do=0x600000, lse=L, dq=0x700000, dk=0x800000, dv=0x900000, B=1, H=1, N=16,
+        d=64, causal=0, scale=0.125, ws=0xA00000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_bytes(B, H, N)
+    return lib.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, N, d, causal, scale, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_bytes(lib):
+    # two float32 statistics per query row, rows padded to a multiple of 64 per head
+    assert lib.fa_bwd_workspace_bytes(1, 1, 1) == 2 * 64 * 4
+    assert lib.fa_bwd_workspace_bytes(2, 3, 65) == 2 * 6 * 128 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 32, 8192) == 2 * 32 * 8192 * 4
+    assert lib.fa_bwd_workspace_bytes(0, 1, 16) == 0 and lib.fa_bwd_workspace_bytes(1, 1, -1) == 0
+
+
+def test_bwd_validation(lib):
+    assert bwd(lib, d=96) == UNSUPPORTED
+    assert bwd(lib, scale=-1.0) == INVALID
+    assert bwd(lib, scale=float("nan")) == INVALID
+    assert bwd(lib, N=-1) == INVALID
+    assert bwd(lib, do=0) == INVALID and bwd(lib, lse=0) == INVALID
+    assert bwd(lib, dq=0) == INVALID and bwd(lib, dk=0) == INVALID and bwd(lib, dv=0) == INVALID
+    assert bwd(lib, ws=0) == INVALID
+    assert bwd(lib, ws_bytes=lib.fa_bwd_workspace_bytes(1, 1, 16) - 4) == INVALID  # too small
+    assert bwd(lib, do=0x600002) == INVALID and bwd(lib, dk=0x800008) == INVALID   # misaligned
+    assert bwd(lib, ws=0xA00004) == INVALID
+    assert bwd(lib, dq=A) == INVALID            # output aliases q
+    assert bwd(lib, dv=0x700000) == INVALID      # dv aliases dq
+    assert bwd(lib, dk=0x600000) == INVALID      # dk aliases dout
+    assert bwd(lib, ws=0x900000) == INVALID      # workspace aliases dv
+    assert bwd(lib, B=0) == FA_OK and bwd(lib, N=0, ws=0, ws_bytes=0) == FA_OK   # empty problem: nothing enqueued
