@@ -77,6 +77,35 @@ def cpu_baseline(w, target_s: float):
                       f"{elapsed:.1f} s"}
 
 
+def backward_leg(fa, torch, si, w, q, k, v, o, lse, steps):
+    """Backward pass (recompute method) at the prefill workload, timed with HIP
+    events on the launch stream; reported apart from the step's value."""
+    dout = torch.from_numpy(si.upstream_grad(w.wid, w.B, w.H, w.N, w.d, "bf16").view("int16")).view(
+        torch.bfloat16).to(q.device)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N) // 4, dtype=torch.float32, device=q.device)
+    fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+    stream = torch.cuda.current_stream(q.device)
+    for _ in range(2):
+        fa.bwd(q, k, v, o, dout, lse, causal=True, scale=w.scale, out=grads, workspace=ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fa.bwd(q, k, v, o, dout, lse, causal=True, scale=w.scale, out=grads, workspace=ws)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    avg = sum(ms) / len(ms)
+    flops = 10 * w.d * w.B * w.H * (w.N * (w.N + 1) // 2)   # S recomputed, dP, dV, dQ, dK: 2 d each per pair
+    assert all(torch.isfinite(g.float()).all().item() for g in grads)
+    return {"value": round(flops / (avg * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms": round(avg, 4),
+            "ms_min": round(min(ms), 4), "flop_per_call": flops, "frac_of_bf16_peak": round(
+                flops / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": "bwd_prep_kernel<128> + bwd_dkdv_kernel<128, causal> + bwd_dq_kernel<128, causal>",
+            "workload": "prefill workload, dO ~ N(0,1) seeded"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="CPU work of the oracle baseline (0 disables it)")
+    ap.add_argument("--bwd-steps", type=int, default=10,
+                    help="timed calls of the backward pass (reported apart from the step; 0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
     args = ap.parse_args()
@@ -191,6 +222,8 @@ def main():
                     "compulsory_bytes": fwd_bytes},
         "input_generation_s": round(gen_s, 1),
     }
+    if args.bwd_steps > 0:
+        rec["backward"] = backward_leg(fa, torch, si, wp, q, k, v, o, lse, args.bwd_steps)
     del q, k, v, dq, dk, dv, o, do
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(wp, args.cpu_baseline_seconds)
