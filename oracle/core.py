@@ -29,6 +29,17 @@ What it computes, and where that is defined:
   each chunk yielding (max, sum, unnormalised output), and the chunks merged
   with the same max-and-sum rule.
 * ``decode`` is the plain definition for one query row per head.
+* ``paged_decode`` is ``decode`` over a paged cache: each sequence's keys
+  live in fixed-size pages of a shared pool, located through a block table.
+  The pages name paged decode kernels as what serving engines use for decode
+  ("Describe Flash Attention at a high level", the paragraph on how the
+  kernel is reached through frameworks; "flashattention-memory-bound"
+  (appliedaiprep.com), the follow-up on long-context serving) but give no
+  layout. Reading: pool [num_pages, H, page_size, d]; key j of sequence b is
+  row j % page_size of pool page block_table[b, j // page_size], for
+  j < seq_lens[b]. The oracle gathers those rows into a contiguous cache and
+  applies the plain definition; a sequence of length 0 gives a zero output
+  (reading: an idle batch slot).
 * ``attention_grad`` is the gradient of the plain definition with respect to
   Q, K and V for an upstream gradient dO, written out from the chain rule
   (dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)), dQ = scale dS K,
@@ -46,8 +57,10 @@ Readings where the pages are silent (also listed in the design notes):
   - causal: key j is visible to query i iff j <= i (same N for Q and K);
   - masked logits are -inf before the row max; every row sees key 0.
 
-Pins: every function here is pinned by tests/test_oracle.py against brute
-force, closed forms and invariants (see that file); none is "parity unpinned".
+Pins: every function here is pinned against brute force, closed forms and
+invariants: the forward and decode functions by tests/test_oracle.py, the
+gradients by tests/test_oracle_grad.py and the paged decode by
+tests/test_oracle_paged.py; none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -183,6 +196,52 @@ def split_decode(q, kc, vc, nsplit: int, scale: float | None = None):
     L = sum(wi * l_s for wi, (_, l_s, _) in zip(w, parts))
     o = sum(wi * o_s for wi, (_, _, o_s) in zip(w, parts)) / L
     return o, M + np.log(L)
+
+
+def gather_pages(pool, table_row, length: int) -> np.ndarray:
+    """Rows 0 .. length-1 of one sequence from a page pool, all heads.
+
+    pool: [num_pages, H, page_size, d]; table_row: the sequence's block-table
+    row. Returns [H, length, d]. A page id outside the pool, or a length that
+    needs more pages than the row holds, raises ValueError.
+    """
+    num_pages, H, ps, d = pool.shape
+    n_used = -(-length // ps)
+    if n_used > len(table_row):
+        raise ValueError(f"length {length} needs {n_used} pages, the block table holds {len(table_row)}")
+    out = np.empty((H, length, d), dtype=pool.dtype)
+    for i in range(n_used):
+        page = int(table_row[i])
+        if not 0 <= page < num_pages:
+            raise ValueError(f"page id {page} outside the pool of {num_pages} pages")
+        rows = min(ps, length - i * ps)                    # the last page may be partly filled
+        out[:, i * ps:i * ps + rows] = pool[page, :, :rows]
+    return out
+
+
+def paged_decode(q, k_pages, v_pages, block_table, seq_lens, scale: float | None = None):
+    """One query row per head over a paged cache: gather, then ``decode``.
+
+    q: [B,H,d]; k_pages, v_pages: [num_pages, H, page_size, d];
+    block_table: [B, max_pages] integers; seq_lens: [B]. Returns
+    (o [B,H,d], lse [B,H]); a sequence of length 0 gives o = 0 and
+    lse = -inf.
+    """
+    q = np.asarray(q, np.float64)
+    B, H, d = q.shape
+    o = np.zeros((B, H, np.shape(v_pages)[-1]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        length = int(seq_lens[b])
+        if length < 0:
+            raise ValueError(f"negative sequence length {length}")
+        if length == 0:
+            continue
+        kc = gather_pages(k_pages, block_table[b], length)
+        vc = gather_pages(v_pages, block_table[b], length)
+        o[b:b + 1], lse[b:b + 1] = decode(q[b:b + 1], np.asarray(kc, np.float64)[None],
+                                          np.asarray(vc, np.float64)[None], scale)
+    return o, lse
 
 
 def _head_attention_grad(q, k, v, do, causal: bool, s: float):

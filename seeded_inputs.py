@@ -160,3 +160,59 @@ def upstream_grad(seed: int, B: int, H: int, N: int, d: int, dtype: str) -> np.n
     rng = np.random.Generator(np.random.PCG64([BASE_SEED, 5000 + seed, B, H, N, d]))
     x = rng.standard_normal((B, H, N, d), dtype=np.float32)
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+BF16_NAN_BITS = 0x7FC0
+
+
+def seq_lengths(seed: int, B: int, Lmax: int, page_size: int) -> np.ndarray:
+    """Seeded ragged cache lengths in [1, Lmax] for paged-decode tests.
+
+    The first entries take edge values that cut pages at every place (one key,
+    one page minus one key, one full page, one page plus one key, Lmax), the
+    rest are uniform draws; values above Lmax are clipped.
+    """
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 6000 + seed, B, Lmax, page_size]))
+    lens = rng.integers(1, Lmax + 1, size=B)
+    edges = [1, page_size - 1, page_size, page_size + 1, Lmax]
+    for i, e in enumerate(edges[:B]):
+        lens[i] = e
+    return np.clip(lens, 1, Lmax).astype(np.int32)
+
+
+def page_cache(seed: int, kc: np.ndarray, vc: np.ndarray, seq_lens, page_size: int, spare_pages: int = 3):
+    """Scatter contiguous caches into a shuffled page pool (layout only, no arithmetic).
+
+    kc, vc: [B, H, Lmax, d] kernel inputs. Returns (k_pages, v_pages,
+    block_table, seq_lens): pools [num_pages, H, page_size, d] of the same
+    dtype, block_table int32 [B, ceil(Lmax / page_size)] and seq_lens int32.
+    Sequence b's key j (j < seq_lens[b]) is row j % page_size of pool page
+    block_table[b, j // page_size]. Pool pages are handed out in a seeded
+    random order; every pool row that holds no key (the tail of a partly
+    filled page, spare pages) is NaN, and block-table entries past a
+    sequence's last page are -1, so reading either shows up.
+    """
+    B, H, Lmax, d = kc.shape
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (B,) or lens.min(initial=0) < 0 or lens.max(initial=0) > Lmax:
+        raise ValueError("seq_lens must be [B] values in [0, Lmax]")
+    max_pages = -(-Lmax // page_size)
+    used = [-(-int(n) // page_size) for n in lens]
+    num_pages = sum(used) + spare_pages
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 7000 + seed, B, H, Lmax, d, page_size]))
+    order = rng.permutation(num_pages)
+    filler = np.uint16(BF16_NAN_BITS) if kc.dtype == np.uint16 else np.float32(np.nan)
+    pools = [np.full((num_pages, H, page_size, d), filler, dtype=kc.dtype) for _ in range(2)]
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        n, pages = int(lens[b]), order[cursor:cursor + used[b]]
+        cursor += used[b]
+        table[b, :used[b]] = pages
+        full = n // page_size
+        for pool, src in zip(pools, (kc, vc)):
+            if full:
+                pool[pages[:full]] = src[b, :, :full * page_size].reshape(H, full, page_size, d).transpose(1, 0, 2, 3)
+            if n % page_size:
+                pool[pages[full], :, :n % page_size] = src[b, :, full * page_size:n]
+    return pools[0], pools[1], table, lens
