@@ -11,6 +11,9 @@ Prints one JSON line: `value` is the prefill's attention-forward throughput
 (algorithmic FLOPs / average prefill time), with a `roofline` entry for the
 fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
 throughput on a bounded sample of the prefill workload in `cpu_baseline`.
+After the timed steps, the same decode over a paged cache (`paged_decode`)
+and the backward pass on the prefill workload (`backward`) are timed on their
+own and reported apart from `value`.
 """
 from __future__ import annotations
 
@@ -106,6 +109,46 @@ def backward_leg(fa, torch, si, w, q, k, v, o, lse, steps):
             "workload": "prefill workload, dO ~ N(0,1) seeded"}
 
 
+def paged_decode_leg(fa, torch, si, wd, dq, dk, dv, steps, page_size=16):
+    """Decode workload with the caches in 16-key pages of a shuffled pool (the
+    seeded block table of the paged-cache generator, pool built on the device),
+    timed with HIP events like the contiguous decode; reported apart."""
+    import numpy as np
+    B, H, L, d = wd.B, wd.H, wd.Lkv, wd.d
+    P = L // page_size
+    table, num_pages = si.page_table(wd.wid, B, H, L, d, np.full(B, L), page_size)
+    idx = torch.from_numpy(table.reshape(-1).astype(np.int64)).to(dq.device)
+    pools = []
+    for c in (dk, dv):
+        pool = torch.full((num_pages, H, page_size, d), float("nan"), dtype=torch.bfloat16, device=dq.device)
+        pool[idx] = c.view(B, H, P, page_size, d).permute(0, 2, 1, 3, 4).reshape(B * P, H, page_size, d)
+        pools.append(pool)
+    tab = torch.from_numpy(table).to(dq.device)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dq.device)
+    out = torch.empty_like(dq)
+    stream = torch.cuda.current_stream(dq.device)
+    for _ in range(2):
+        fa.decode_paged(dq, pools[0], pools[1], tab, lens, nsplit=wd.nsplit, out=out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fa.decode_paged(dq, pools[0], pools[1], tab, lens, nsplit=wd.nsplit, out=out)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    avg = sum(ms) / len(ms)
+    nbytes = 2 * B * H * L * d * 2 + 2 * B * H * d * 2 + B * P * 4 + B * 4   # K, V pages + q, o + table + lengths
+    assert torch.isfinite(out.float()).all().item()
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    del pools
+    return {"value": round(gbps, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "ms": round(avg, 4), "ms_min": round(min(ms), 4), "algorithmic_bytes_per_call": nbytes,
+            "page_size": page_size, "num_pages": num_pages,
+            "kernels": "decode_split_paged_kernel<128> + decode_combine_kernel<128>",
+            "workload": "decode workload, pages of a shuffled pool (seeded block table), every sequence full"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +158,8 @@ def main():
                     help="CPU work of the oracle baseline (0 disables it)")
     ap.add_argument("--bwd-steps", type=int, default=10,
                     help="timed calls of the backward pass (reported apart from the step; 0 disables it)")
+    ap.add_argument("--paged-steps", type=int, default=20,
+                    help="timed calls of the paged-KV decode (reported apart from the step; 0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
     args = ap.parse_args()
@@ -222,6 +267,8 @@ def main():
                     "compulsory_bytes": fwd_bytes},
         "input_generation_s": round(gen_s, 1),
     }
+    if args.paged_steps > 0:
+        rec["paged_decode"] = paged_decode_leg(fa, torch, si, wd, dq, dk, dv, args.paged_steps)
     if args.bwd_steps > 0:
         rec["backward"] = backward_leg(fa, torch, si, wp, q, k, v, o, lse, args.bwd_steps)
     del q, k, v, dq, dk, dv, o, do

@@ -26,6 +26,7 @@ SIGNATURES = {
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "fa_bwd_workspace_bytes": (_S, [_I, _I, _I]),
     "fa_naive_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
@@ -139,6 +140,37 @@ def decode(q, kcache, vcache, nsplit: int = 64, out=None):
     with torch.cuda.device(q.device):
         st = lib.fa_decode(_ptr(q3), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d, int(nsplit), _stream(q))
     _check("fa_decode", st)
+    return o
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, nsplit: int = 64, out=None):
+    """Split-KV decode over a paged cache.
+
+    q: [B,H,d] (or [B,H,1,d]) bf16; k_pages, v_pages: [num_pages,H,page_size,d]
+    bf16 pools; block_table: int32 [B,max_pages] and seq_lens: int32 [B], both
+    on the device. Returns o like q.
+    """
+    lib = load()
+    q3 = q.reshape(q.shape[0], q.shape[1], q.shape[-1]) if q.dim() == 4 else q
+    for name, t in (("q", q3), ("k_pages", k_pages), ("v_pages", v_pages)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32:
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if q3.dim() != 3 or k_pages.dim() != 4 or k_pages.shape != v_pages.shape or block_table.dim() != 2:
+        raise ValueError("q must be [B,H,d], the pools [num_pages,H,page_size,d], block_table [B,max_pages]")
+    B, H, d = q3.shape
+    num_pages, ph, page_size, pd = k_pages.shape
+    if ph != H or pd != d or block_table.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("pool, table or length shapes do not match q")
+    o = torch.empty_like(q) if out is None else out
+    if o.numel() != q3.numel() or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor like q")
+    with torch.cuda.device(q.device):
+        st = lib.fa_decode_paged(_ptr(q3), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+                                 B, H, d, page_size, num_pages, block_table.shape[1], int(nsplit), _stream(q))
+    _check("fa_decode_paged", st)
     return o
 
 

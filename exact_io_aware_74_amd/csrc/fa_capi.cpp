@@ -78,6 +78,34 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+// The decode partials buffer of (current device, stream), grown to `need`
+// bytes if smaller. Growing synchronises the stream first: earlier decodes on
+// it may still read the old buffer.
+static int decode_workspace(void* stream, size_t need, float** ws) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& w = g_ws[{dev, (hipStream_t)stream}];
+  if (w.bytes < need) {
+    if (w.ptr) {
+      e = hipStreamSynchronize((hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e);
+      (void)hipFree(w.ptr);
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if (hipMalloc(&w.ptr, need) != hipSuccess) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return FA_ERR_NOMEM;
+    }
+    w.bytes = need;
+  }
+  *ws = (float*)w.ptr;
+  return FA_OK;
+}
+
 static void decode_split_shape(int Lkv, int nsplit, int* chunk, int* nsplit_eff) {
   const int n = nsplit < Lkv ? nsplit : Lkv;
   *chunk = (Lkv + n - 1) / n;
@@ -106,33 +134,41 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o, in
   if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, kcache, cbytes) || overlaps(o, qbytes, vcache, cbytes))
     return FA_ERR_INVALID_ARG;
 
-  const size_t need = fa_decode_workspace_bytes(B, H, Lkv, d, nsplit);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e);
   float* ws = nullptr;
-  {
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, (hipStream_t)stream}];
-    if (w.bytes < need) {
-      if (w.ptr) {
-        // earlier decodes on this stream may still read the old buffer
-        e = hipStreamSynchronize((hipStream_t)stream);
-        if (e != hipSuccess) return hip_fail(e);
-        (void)hipFree(w.ptr);
-        w.ptr = nullptr;
-        w.bytes = 0;
-      }
-      if (hipMalloc(&w.ptr, need) != hipSuccess) {
-        (void)hipGetLastError();
-        w.ptr = nullptr;
-        return FA_ERR_NOMEM;
-      }
-      w.bytes = need;
-    }
-    ws = (float*)w.ptr;
-  }
-  e = fa::launch_decode(q, kcache, vcache, o, ws, B, H, Lkv, d, ns, chunk, (hipStream_t)stream);
+  const int st = decode_workspace(stream, fa_decode_workspace_bytes(B, H, Lkv, d, nsplit), &ws);
+  if (st != FA_OK) return st;
+  const hipError_t e = fa::launch_decode(q, kcache, vcache, o, ws, B, H, Lkv, d, ns, chunk, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                    const int32_t* seq_lens, void* o, int B, int H, int d, int page_size, int num_pages,
+                    int max_pages, int nsplit, void* stream) {
+  if (B < 0 || H < 0 || d <= 0 || num_pages <= 0 || max_pages <= 0 || nsplit <= 0) return FA_ERR_INVALID_ARG;
+  if (page_size <= 0 || page_size > 65536 || (page_size & (page_size - 1))) return FA_ERR_INVALID_ARG;
+  if ((int64_t)max_pages * page_size > (int64_t)1 << 30) return FA_ERR_INVALID_ARG;  // key indices stay far from INT_MAX
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return FA_OK;
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)block_table & 3u) || ((uintptr_t)seq_lens & 3u)) return FA_ERR_INVALID_ARG;
+  const int lmax = max_pages * page_size;
+  int chunk, ns;
+  decode_split_shape(lmax, nsplit, &chunk, &ns);
+  const int64_t bh = (int64_t)B * H;
+  if (bh * ns > INT_MAX) return FA_ERR_INVALID_ARG;
+  const size_t qbytes = (size_t)bh * d * 2;
+  const size_t pbytes = (size_t)num_pages * (size_t)H * (size_t)page_size * (size_t)d * 2;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k_pages, pbytes) || overlaps(o, qbytes, v_pages, pbytes) ||
+      overlaps(o, qbytes, block_table, (size_t)B * max_pages * 4) || overlaps(o, qbytes, seq_lens, (size_t)B * 4))
+    return FA_ERR_INVALID_ARG;
+  int lps = 0;
+  while ((1 << lps) < page_size) ++lps;
+  float* ws = nullptr;
+  const int st = decode_workspace(stream, fa_decode_workspace_bytes(B, H, lmax, d, nsplit), &ws);
+  if (st != FA_OK) return st;
+  const hipError_t e = fa::launch_decode_paged(q, k_pages, v_pages, block_table, seq_lens, o, ws, B, H, d, lps,
+                                               num_pages, max_pages, ns, chunk, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 

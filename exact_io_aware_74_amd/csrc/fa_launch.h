@@ -17,6 +17,13 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* ws,
                          int B, int H, int Lkv, int d, int nsplit, int chunk, hipStream_t s);
 
+// Paged decode: pools [num_pages, H, 2^log2_page, d], table [B, max_pages],
+// lens [B] (device). Splits cover `chunk` keys of max_pages * 2^log2_page;
+// splits past a sequence's length are empty. `ws` as for launch_decode.
+hipError_t launch_decode_paged(const void* q, const void* kpool, const void* vpool, const int* table, const int* lens,
+                               void* o, float* ws, int B, int H, int d, int log2_page, int num_pages, int max_pages,
+                               int nsplit, int chunk, hipStream_t s);
+
 // Backward with recompute: dq, dk, dv from q, k, v, o, dout and the forward's
 // lse. `ws` holds 2 * B*H*bwd_rows_padded(N) floats.
 int bwd_rows_padded(int N);

@@ -33,6 +33,7 @@
 #define FA_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -103,6 +104,43 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o,
 
 /* Bytes of decode partials for this shape (the buffer fa_decode keeps). */
 size_t fa_decode_workspace_bytes(int B, int H, int Lkv, int d, int nsplit);
+
+/*
+ * fa_decode_paged -- fa_decode over a paged KV cache: the keys of each
+ * sequence live in fixed-size pages of a shared pool, found through a block
+ * table, as the decode kernels of serving engines keep them. Sources:
+ * mantramindai.in, the paragraph on how the kernel is reached through
+ * frameworks (paged variants for decode); appliedaiprep.com, the follow-up on
+ * long-context serving. The pages give no layout; this one keeps each
+ * (page, head) contiguous.
+ *
+ *   q               const bf16 [B,H,d]
+ *   k_pages,
+ *   v_pages         const bf16 [num_pages, H, page_size, d] (the pools)
+ *   block_table     const int32 [B, max_pages], device memory: key j of
+ *                   sequence b is row j % page_size of pool page
+ *                   block_table[b][j / page_size]; entries past a sequence's
+ *                   last page are never read
+ *   seq_lens        const int32 [B], device memory: keys per sequence, in
+ *                   [0, max_pages * page_size]
+ *   o               bf16 [B,H,d]
+ *   page_size       a power of two, 1 .. 65536
+ *   num_pages, max_pages, nsplit >= 1; max_pages * page_size <= 2^30
+ *   d               64 or 128
+ * The cache is split as fa_decode splits a cache of Lkv = max_pages *
+ * page_size keys; splits past a sequence's length contribute nothing. The
+ * logit scale is 1/sqrt(d) (rounded to float32). Values that live in device
+ * memory are checked by the kernels, which never read outside the pool or the
+ * table: a sequence of length 0 gives o = 0; a length outside the range, or a
+ * page id outside [0, num_pages) among a sequence's pages, gives NaN in that
+ * sequence's rows of o. Host-side arguments are checked as in fa_decode;
+ * overlap of o with any input is FA_ERR_INVALID_ARG. Workspace: the same
+ * library-owned buffer as fa_decode, fa_decode_workspace_bytes(B, H,
+ * max_pages * page_size, d, nsplit) bytes.
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                    const int32_t* seq_lens, void* o, int B, int H, int d, int page_size, int num_pages,
+                    int max_pages, int nsplit, void* stream);
 
 /*
  * fa_bwd -- gradients of fa_fwd with respect to Q, K and V, computed with the

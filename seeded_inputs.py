@@ -180,6 +180,28 @@ def seq_lengths(seed: int, B: int, Lmax: int, page_size: int) -> np.ndarray:
     return np.clip(lens, 1, Lmax).astype(np.int32)
 
 
+def page_table(seed: int, B: int, H: int, Lmax: int, d: int, seq_lens, page_size: int, spare_pages: int = 3):
+    """The block table of ``page_cache`` alone: (table int32 [B, ceil(Lmax / page_size)], num_pages).
+
+    Sequence b takes ceil(seq_lens[b] / page_size) pool pages, handed out in a
+    seeded random order; entries past its last page are -1.
+    """
+    lens = np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (B,) or lens.min(initial=0) < 0 or lens.max(initial=0) > Lmax:
+        raise ValueError("seq_lens must be [B] values in [0, Lmax]")
+    max_pages = -(-Lmax // page_size)
+    used = [-(-int(n) // page_size) for n in lens]
+    num_pages = sum(used) + spare_pages
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 7000 + seed, B, H, Lmax, d, page_size]))
+    order = rng.permutation(num_pages)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    cursor = 0
+    for b in range(B):
+        table[b, :used[b]] = order[cursor:cursor + used[b]]
+        cursor += used[b]
+    return table, num_pages
+
+
 def page_cache(seed: int, kc: np.ndarray, vc: np.ndarray, seq_lens, page_size: int, spare_pages: int = 3):
     """Scatter contiguous caches into a shuffled page pool (layout only, no arithmetic).
 
@@ -194,21 +216,12 @@ def page_cache(seed: int, kc: np.ndarray, vc: np.ndarray, seq_lens, page_size: i
     """
     B, H, Lmax, d = kc.shape
     lens = np.asarray(seq_lens, dtype=np.int32)
-    if lens.shape != (B,) or lens.min(initial=0) < 0 or lens.max(initial=0) > Lmax:
-        raise ValueError("seq_lens must be [B] values in [0, Lmax]")
-    max_pages = -(-Lmax // page_size)
-    used = [-(-int(n) // page_size) for n in lens]
-    num_pages = sum(used) + spare_pages
-    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 7000 + seed, B, H, Lmax, d, page_size]))
-    order = rng.permutation(num_pages)
+    table, num_pages = page_table(seed, B, H, Lmax, d, lens, page_size, spare_pages)
     filler = np.uint16(BF16_NAN_BITS) if kc.dtype == np.uint16 else np.float32(np.nan)
     pools = [np.full((num_pages, H, page_size, d), filler, dtype=kc.dtype) for _ in range(2)]
-    table = np.full((B, max_pages), -1, dtype=np.int32)
-    cursor = 0
     for b in range(B):
-        n, pages = int(lens[b]), order[cursor:cursor + used[b]]
-        cursor += used[b]
-        table[b, :used[b]] = pages
+        n = int(lens[b])
+        pages = table[b, :-(-n // page_size)]
         full = n // page_size
         for pool, src in zip(pools, (kc, vc)):
             if full:

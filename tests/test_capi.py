@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
-              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes"):
+              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_paged"):
         assert n in names
     assert len(names) == len(set(names))
 
@@ -89,6 +89,35 @@ def test_decode_validation(lib):
     assert dec(v=C + 4) == INVALID
     assert dec(o=Bp) == INVALID                                      # output inside the K cache
     assert dec(B=0, q=0, k=0, v=0, o=0) == FA_OK
+
+
+T = 0x600000
+S = 0x700000
+
+
+def test_decode_paged_validation(lib):
+    def dec(**kw):
+        return lib.fa_decode_paged(kw.get("q", A), kw.get("k", Bp), kw.get("v", C), kw.get("table", T),
+                                   kw.get("lens", S), kw.get("o", Dp), kw.get("B", 2), kw.get("H", 2),
+                                   kw.get("d", 128), kw.get("page_size", 16), kw.get("num_pages", 8),
+                                   kw.get("max_pages", 4), kw.get("nsplit", 4), None)
+    assert dec(d=80) == UNSUPPORTED
+    for bad in (0, -16, 12, 3, 1 << 17):                            # not a power of two in 1 .. 65536
+        assert dec(page_size=bad) == INVALID
+    assert dec(num_pages=0) == INVALID
+    assert dec(max_pages=0) == INVALID
+    assert dec(nsplit=0) == INVALID
+    assert dec(max_pages=1 << 16, page_size=1 << 15) == INVALID      # more than 2^30 keys per sequence
+    assert dec(table=0) == INVALID
+    assert dec(lens=0) == INVALID
+    assert dec(table=T + 2) == INVALID                               # misaligned int32 table
+    assert dec(lens=S + 1) == INVALID
+    assert dec(k=Bp + 8) == INVALID
+    assert dec(o=T) == INVALID                                       # output over the block table
+    assert dec(o=Bp + 64) == INVALID                                 # output inside the K pool
+    assert dec(o=S) == INVALID                                       # output over the lengths
+    assert dec(B=0, q=0, k=0, v=0, table=0, lens=0, o=0) == FA_OK
+    assert dec(H=0) == FA_OK
 
 
 def test_decode_workspace_size(lib):
