@@ -11,9 +11,10 @@ Prints one JSON line: `value` is the prefill's attention-forward throughput
 (algorithmic FLOPs / average prefill time), with a `roofline` entry for the
 fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
 throughput on a bounded sample of the prefill workload in `cpu_baseline`.
-After the timed steps, the same decode over a paged cache (`paged_decode`)
-and the backward pass on the prefill workload (`backward`) are timed on their
-own and reported apart from `value`.
+After the timed steps, the same decode over a paged cache (`paged_decode`),
+the backward pass on the prefill workload (`backward`) and a 128K-token
+prefill (`long_prefill`) are timed on their own and reported apart from
+`value`.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the pub
 PEAK_HBM_GBPS = 8000.0       # published HBM3E bandwidth
 PREFILL = "bf16_h32_n8192_d128_causal_k2"
 DECODE = "decode_b16h32_l32768_d128"
+LONG = "bf16_b4h32_n131072_d128_causal"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_n8192.json")
 FWD_SOURCES = [os.path.join(ROOT, "exact_io_aware_74_amd", "csrc", f) for f in ("fa_fwd_bf16.hip", "fa_device.h")]
 
@@ -149,6 +151,37 @@ def paged_decode_leg(fa, torch, si, wd, dq, dk, dv, steps, page_size=16):
             "workload": "decode workload, pages of a shuffled pool (seeded block table), every sequence full"}
 
 
+def long_prefill_leg(fa, torch, si, steps):
+    """The 128K-token causal prefill (B=4, H=32, N=131072, d=128, bf16), inputs
+    N(0,1) from a seeded device generator, timed with HIP events; reported apart."""
+    w = si.WORKLOADS[LONG]
+    gen = torch.Generator(device="cuda").manual_seed(w.wid)
+    shape = (w.B, w.H, w.N, w.d)
+    q, k, v = (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    avg = sum(ms) / len(ms)
+    flops = 4 * w.d * w.B * w.H * (w.N * (w.N + 1) // 2)
+    assert torch.isfinite(lse).all().item()
+    del q, k, v, o, lse
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "ms": round(avg, 3), "ms_min": round(min(ms), 3), "flop_per_call": flops,
+            "kernel": "fwd_bf16_kernel<128, causal>",
+            "workload": "prefill B=4 H=32 N=131072 d=128 bf16 causal, N(0,1) inputs from a seeded device generator"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -160,6 +193,8 @@ def main():
                     help="timed calls of the backward pass (reported apart from the step; 0 disables it)")
     ap.add_argument("--paged-steps", type=int, default=20,
                     help="timed calls of the paged-KV decode (reported apart from the step; 0 disables it)")
+    ap.add_argument("--long-steps", type=int, default=3,
+                    help="timed calls of the 128K-token prefill (reported apart from the step; 0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
     args = ap.parse_args()
@@ -272,6 +307,8 @@ def main():
     if args.bwd_steps > 0:
         rec["backward"] = backward_leg(fa, torch, si, wp, q, k, v, o, lse, args.bwd_steps)
     del q, k, v, dq, dk, dv, o, do
+    if args.long_steps > 0:
+        rec["long_prefill"] = long_prefill_leg(fa, torch, si, args.long_steps)
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(wp, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)

@@ -52,7 +52,7 @@ class Workload:
         return self.Lkv if self.decode else self.N
 
 
-# The five workloads of this library's test and benchmark plan.
+# The workloads of this library's test and benchmark plan.
 WORKLOADS = {
     "f32_n256_d64": Workload(1, "f32_n256_d64", 1, 1, 256, 64, "f32", False),
     "bf16_b4h16_n1024_d64_causal": Workload(2, "bf16_b4h16_n1024_d64_causal", 4, 16, 1024, 64, "bf16", True),
@@ -61,6 +61,8 @@ WORKLOADS = {
     "bf16_h32_n16384_d128_causal": Workload(4, "bf16_h32_n16384_d128_causal", 1, 32, 16384, 128, "bf16", True),
     "decode_b16h32_l32768_d128": Workload(5, "decode_b16h32_l32768_d128", 16, 32, 1, 128, "bf16", False,
                                           decode=True, Lkv=32768, nsplit=64),
+    "bf16_b4h32_n131072_d128_causal": Workload(6, "bf16_b4h32_n131072_d128_causal", 4, 32, 131072, 128, "bf16",
+                                               True),
 }
 
 

@@ -58,7 +58,32 @@ def test_workload_long_prefill_sampled(name):
     print(name, _fwd_case(q, k, v, "bf16", w.causal, w.scale, rows=rows, heads=heads))
 
 
-@pytest.mark.parametrize("name", ["bf16_h32_n8192_d128_causal_k2", "bf16_h32_n16384_d128_causal"])
+def test_workload_128k_prefill_sampled():
+    """128K-token causal prefill, B=4 x H=32: each tensor holds 2^31 elements, so element offsets
+    of the later heads pass 2^31. Sampled rows of heads at both ends against the oracle; only those
+    rows leave the device."""
+    w = W["bf16_b4h32_n131072_d128_causal"]
+    q, k, v = workload_inputs(w)
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    o, lse = fa.fwd(qd, kd, vd, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.N, 48, seed=w.wid, tile=256)
+    ridx = torch.tensor(rows, device="cuda")
+    got_o, got_l, ref_o, ref_l = [], [], [], []
+    for b, h in [(0, 0), (1, 17), (3, 30), (3, 31)]:
+        got_o.append(to_f64(o[b, h].index_select(0, ridx)))
+        got_l.append(to_f64(lse[b, h].index_select(0, ridx)))
+        one = lambda x: si.as_float64(x[b:b + 1, h:h + 1], "bf16")
+        O, L = oracle.attention(one(q), one(k), one(v), True, w.scale, rows=rows)
+        ref_o.append(O[0, 0])
+        ref_l.append(L[0, 0])
+    print("128K", assert_close(np.stack(got_o), np.stack(ref_o), "bf16"),
+          assert_lse_close(np.stack(got_l), np.stack(ref_l), "bf16"))
+    assert torch.isfinite(o[3, 31]).all().item()
+
+
+@pytest.mark.parametrize("name", ["bf16_h32_n8192_d128_causal_k2", "bf16_h32_n16384_d128_causal",
+                                  "bf16_b4h32_n131072_d128_causal"])
 def test_fused_pass_allocates_nothing(name):
     """The fused pass needs no workspace: device memory is unchanged across the
     call (an N x N score buffer would be 1 GiB per head at N = 16384)."""
