@@ -231,3 +231,84 @@ def page_cache(seed: int, kc: np.ndarray, vc: np.ndarray, seq_lens, page_size: i
             if n % page_size:
                 pool[pages[full], :, :n % page_size] = src[b, :, full * page_size:n]
     return pools[0], pools[1], table, lens
+
+
+# ---- FP8 (OCP e4m3, "fn": no infinities, 0x7F / 0xFF are NaN, largest finite 448) ----
+E4M3_MAX = 448.0
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to e4m3 with round-to-nearest-even; returns uint8 codes.
+
+    Values beyond the largest finite code after rounding are rejected (the
+    inputs are scaled into range first); subnormals (steps of 2^-9 below
+    2^-6) are rounded like normals.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if not np.isfinite(x).all():
+        raise ValueError("f32_to_e4m3_bits expects finite inputs")
+    a = np.abs(x).astype(np.float64)
+    _, ef = np.frexp(a)                                   # a = f * 2^ef, f in [0.5, 1)
+    e = np.maximum(ef.astype(np.int64) - 1, -6)           # exponent of the leading bit; subnormals share -6
+    q = np.rint(a * np.exp2(3 - e))                       # 3 mantissa bits: exact scaling, ties to even
+    carry = q >= 16
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, 8, q).astype(np.int64)
+    code = np.where(q < 8, q, ((e + 7) << 3) | (q - 8))
+    if (code > 0x7E).any():
+        raise ValueError("value out of the e4m3 range")
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def e4m3_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact decoding of e4m3 codes (NaN for 0x7F and 0xFF)."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    ef, m = (b >> 3) & 15, b & 7
+    val = np.where(ef == 0, m * 2.0 ** -9, (8 + m) * np.exp2(ef - 10.0))
+    val = np.where((ef == 15) & (m == 7), np.nan, val)
+    return np.where(b >> 7, -val, val).astype(np.float32)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor FP8 quantisation: descale = max|x| / 448 (float32), codes = e4m3(x / descale).
+
+    The logical tensor is descale * decode(codes)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = float(np.abs(x).max()) if x.size else 0.0
+    descale = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    scaled = np.clip(x / descale, -E4M3_MAX, E4M3_MAX)    # division rounding may step past 448
+    return f32_to_e4m3_bits(scaled), float(descale)
+
+
+def fp8_as_float64(codes: np.ndarray, descale: float) -> np.ndarray:
+    """The logical values of an FP8 tensor, exactly, in float64."""
+    return e4m3_bits_to_f32(codes).astype(np.float64) * np.float64(np.float32(descale))
+
+
+def fp8_case(seed: int, B: int, H: int, N: int, d: int, std: float = 1.0):
+    """Seeded FP8 inputs: q, k ~ std * N(0,1), v ~ N(0,1), each quantised per tensor.
+
+    Returns (q8, k8, v8, (q_descale, k_descale, v_descale))."""
+    rng = np.random.Generator(np.random.PCG64([BASE_SEED, 8000 + seed, B, H, N, d]))
+    outs, scales = [], []
+    for sd in (std, std, 1.0):
+        x = (rng.standard_normal((B, H, N, d), dtype=np.float32) * np.float32(sd)).astype(np.float32)
+        codes, ds = quantize_e4m3(x)
+        outs.append(codes)
+        scales.append(ds)
+    return outs[0], outs[1], outs[2], tuple(scales)
+
+
+def fp8_workload(w: Workload):
+    """A workload's Q, K, V draws (the same float32 values as its bf16 inputs before the
+    bf16 cast), quantised to FP8 per tensor. Returns (q8, k8, v8, descales)."""
+    outs, scales = [], []
+    for t in ("q", "k", "v"):
+        x = np.empty((w.B, w.H, w.N, w.d), dtype=np.float32)
+        for b in range(w.B):
+            for h in range(w.H):
+                x[b, h] = _slice_values(w, t, b, h, w.N)
+        codes, ds = quantize_e4m3(x)
+        outs.append(codes)
+        scales.append(ds)
+    return outs[0], outs[1], outs[2], tuple(scales)

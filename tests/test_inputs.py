@@ -55,3 +55,38 @@ def test_workload_table():
     assert si.tensor_slice(d, "q", 0, 0).shape == (1, 128)
     x = si.tensor_slice(w, "q", 0, 0)
     assert x.dtype == np.float32 and abs(float(x.std()) - 1.0) < 0.05
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(200_000).astype(np.float32) * 60,
+                        np.float32(2.0) ** rng.uniform(-14, 8.8, 100_000).astype(np.float32),
+                        np.float32([0.0, -0.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 2.0 ** -6])])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    # exact ties between neighbouring codes, both signs
+    codes = torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    mids = ((codes[:-1] + codes[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids])
+    ours = si.f32_to_e4m3_bits(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_decoder_exact_on_every_code():
+    bits = np.arange(256, dtype=np.uint8)
+    ours = si.e4m3_bits_to_f32(bits)
+    ref = torch.from_numpy(bits).view(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(ours, ref)                 # NaN positions compare equal here
+    finite = np.isfinite(ours)
+    np.testing.assert_array_equal(si.f32_to_e4m3_bits(ours[finite]), bits[finite])
+
+
+def test_fp8_quantisation_recipe():
+    q8, k8, v8, (dq, dk, dv) = si.fp8_case(3, 1, 2, 100, 128, std=2.0)
+    assert q8.dtype == np.uint8 and q8.shape == (1, 2, 100, 128)
+    for codes, ds in ((q8, dq), (k8, dk), (v8, dv)):
+        vals = si.fp8_as_float64(codes, ds)
+        assert np.isclose(np.abs(vals).max(), 448 * ds, rtol=2 ** -4)   # the largest element maps to ~448
+        assert ds == float(np.float32(ds))
+    a = si.fp8_case(3, 1, 2, 100, 128, std=2.0)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], (q8, k8, v8)))
