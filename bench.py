@@ -12,9 +12,9 @@ Prints one JSON line: `value` is the prefill's attention-forward throughput
 fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
 throughput on a bounded sample of the prefill workload in `cpu_baseline`.
 After the timed steps, the same decode over a paged cache (`paged_decode`),
-the backward pass on the prefill workload (`backward`) and a 128K-token
-prefill (`long_prefill`) are timed on their own and reported apart from
-`value`.
+the backward pass on the prefill workload (`backward`), the FP8 forward on the
+prefill workload (`fp8_prefill`) and a 128K-token prefill (`long_prefill`)
+are timed on their own and reported apart from `value`.
 """
 from __future__ import annotations
 
@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) at N=8K d=128; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the published 2.5 PFLOP/s dense)
 PEAK_HBM_GBPS = 8000.0       # published HBM3E bandwidth
+PEAK_FP8_TFLOPS = 5033.2     # dense FP8 MFMA: twice the bf16 rate (the published 5.0 PFLOP/s)
 PREFILL = "bf16_h32_n8192_d128_causal_k2"
 DECODE = "decode_b16h32_l32768_d128"
 LONG = "bf16_b4h32_n131072_d128_causal"
@@ -151,6 +152,36 @@ def paged_decode_leg(fa, torch, si, wd, dq, dk, dv, steps, page_size=16):
             "workload": "decode workload, pages of a shuffled pool (seeded block table), every sequence full"}
 
 
+def fp8_prefill_leg(fa, torch, si, w, steps):
+    """The prefill workload's draws quantised per tensor to FP8 e4m3, through the FP8
+    forward; timed with HIP events, reported apart (peak: the dense FP8 MFMA rate)."""
+    import numpy as np
+    q8, k8, v8, ds = si.fp8_workload(w)
+    q, k, v = (torch.from_numpy(x).cuda() for x in (q8, k8, v8))
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fa.fwd_fp8(q, k, v, ds, causal=True, scale=w.scale, out=o, lse=lse)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        fa.fwd_fp8(q, k, v, ds, causal=True, scale=w.scale, out=o, lse=lse)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    avg = sum(ms) / len(ms)
+    flops = 4 * w.d * w.B * w.H * (w.N * (w.N + 1) // 2)
+    assert torch.isfinite(o.float()).all().item()
+    del q, k, v, o, lse
+    tf = flops / (avg * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "ms": round(avg, 4), "ms_min": round(min(ms), 4), "flop_per_call": flops,
+            "kernel": "fwd_fp8_kernel<causal>",
+            "workload": "prefill workload (B=1 H=32 N=8192 d=128 causal, K x2) quantised per tensor to e4m3"}
+
+
 def long_prefill_leg(fa, torch, si, steps):
     """The 128K-token causal prefill (B=4, H=32, N=131072, d=128, bf16), inputs
     N(0,1) from a seeded device generator, timed with HIP events; reported apart."""
@@ -193,6 +224,8 @@ def main():
                     help="timed calls of the backward pass (reported apart from the step; 0 disables it)")
     ap.add_argument("--paged-steps", type=int, default=20,
                     help="timed calls of the paged-KV decode (reported apart from the step; 0 disables it)")
+    ap.add_argument("--fp8-steps", type=int, default=20,
+                    help="timed calls of the FP8 forward on the prefill workload (reported apart; 0 disables it)")
     ap.add_argument("--long-steps", type=int, default=3,
                     help="timed calls of the 128K-token prefill (reported apart from the step; 0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -307,6 +340,8 @@ def main():
     if args.bwd_steps > 0:
         rec["backward"] = backward_leg(fa, torch, si, wp, q, k, v, o, lse, args.bwd_steps)
     del q, k, v, dq, dk, dv, o, do
+    if args.fp8_steps > 0:
+        rec["fp8_prefill"] = fp8_prefill_leg(fa, torch, si, wp, args.fp8_steps)
     if args.long_steps > 0:
         rec["long_prefill"] = long_prefill_leg(fa, torch, si, args.long_steps)
     if args.cpu_baseline_seconds > 0:

@@ -24,6 +24,7 @@ _P, _I, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "fa_fwd_f32": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
@@ -119,6 +120,31 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
                               scale, _stream(q))
     _check(fn, st)
     return o, lse
+
+
+def fwd_fp8(q, k, v, descales, causal: bool = False, scale: float | None = None, out=None, lse=None,
+            return_lse: bool = True):
+    """Fused forward on FP8 (e4m3) inputs. q, k, v: [B,H,N,d] uint8 device tensors holding e4m3 codes
+    (or torch.float8_e4m3fn); descales: (q_descale, k_descale, v_descale). Returns (o bf16, lse float32)."""
+    lib = load()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"{name} must be a contiguous uint8 / float8_e4m3fn device tensor")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must have the same [B,H,N,d] shape")
+    B, H, N, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    qd, kd, vd = (float(x) for x in descales)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device) if out is None else out
+    if o.shape != q.shape or o.dtype != torch.bfloat16 or not o.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of q's shape")
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse if return_lse else None), B, H, N, d,
+                            int(bool(causal)), scale, qd, kd, vd, _stream(q))
+    _check("fa_fwd_fp8", st)
+    return o, (lse if return_lse else None)
 
 
 def decode(q, kcache, vcache, nsplit: int = 64, out=None):

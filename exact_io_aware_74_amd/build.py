@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_bwd.hip", "fa_decode.hip", "fa_naive.hip", "fa_capi.cpp"]
+SOURCES = ["fa_fwd_bf16.hip", "fa_fwd_f32.hip", "fa_fwd_fp8.hip", "fa_bwd.hip", "fa_decode.hip", "fa_naive.hip", "fa_capi.cpp"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -37,7 +37,8 @@ def _run(cmd):
 # asm and wants the compiler's own MFMAs (the scores, read by the softmax) in
 # VGPRs; its copy asm sets M0, which no other instruction of that kernel uses
 # (the warning about clobbering a reserved register is silenced).
-EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"], "fa_bwd.hip": ["-Wno-inline-asm"]}
+EXTRA = {"fa_fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"],
+         "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"], "fa_bwd.hip": ["-Wno-inline-asm"]}
 
 
 def _compile(src: str) -> str:

@@ -81,6 +81,29 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
 // The decode partials buffer of (current device, stream), grown to `need`
 // bytes if smaller. Growing synchronises the stream first: earlier decodes on
 // it may still read the old buffer.
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               int causal, float scale, float q_descale, float k_descale, float v_descale, void* stream) {
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  for (float x : {scale, q_descale, k_descale, v_descale})
+    if (!std::isfinite(x) || x < 0.f) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  if (lse && ((uintptr_t)lse & 3u)) return FA_ERR_INVALID_ARG;
+  const int64_t bh = (int64_t)B * H;
+  if (bh > INT_MAX || bh * (((int64_t)N + 255) / 256) > INT_MAX) return FA_ERR_INVALID_ARG;
+  const size_t in_bytes = (size_t)bh * (size_t)N * (size_t)d, out_bytes = 2 * in_bytes;
+  if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) || overlaps(o, out_bytes, v, in_bytes))
+    return FA_ERR_INVALID_ARG;
+  if (lse && (overlaps(lse, (size_t)bh * N * 4, o, out_bytes) || overlaps(lse, (size_t)bh * N * 4, q, in_bytes) ||
+              overlaps(lse, (size_t)bh * N * 4, k, in_bytes) || overlaps(lse, (size_t)bh * N * 4, v, in_bytes)))
+    return FA_ERR_INVALID_ARG;
+  const hipError_t e = fa::launch_fwd_fp8(q, k, v, o, lse, B, H, N, causal != 0, scale, q_descale, k_descale,
+                                          v_descale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 static int decode_workspace(void* stream, size_t need, float** ws) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

@@ -80,6 +80,31 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /*
+ * fa_fwd_fp8 -- the fused forward with FP8 inputs on the FP8 matrix cores, the
+ * FlashAttention-3 FP8 mode that hassanahmed.net (the section on later
+ * versions) and mantramindai.in (the paragraph on FA-3) mention. The pages fix
+ * no scaling convention; here each input tensor carries one float descale
+ * factor, so the logical inputs are q_descale * Q, k_descale * K and
+ * v_descale * V, and the output is attention of those (same mask and LSE
+ * definition as fa_fwd).
+ *
+ *   q, k, v     const FP8 e4m3 (OCP "fn" encoding, 1 byte) [B,H,N,d]
+ *   o           bf16 [B,H,N,d]
+ *   lse         float32 [B,H,N] or NULL: natural-log LSE of the scaled logits
+ *   d           128 only (FA_ERR_UNSUPPORTED otherwise)
+ *   scale, q_descale, k_descale, v_descale: finite and >= 0
+ * Arithmetic: Q K^T on FP8 MFMAs with fp32 accumulation; the probabilities
+ * are rounded to e4m3 (nearest even, after an exact power-of-two scaling that
+ * keeps them in e4m3's normal range) for the P V product; the row sums use
+ * the fp32 probabilities; O is rounded once to bf16. Each probability carries
+ * a relative error of at most 2^-4, so |O - exact| <= (2^-4 + 2^-9) max|V|.
+ * Errors and alignment as fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale,
+               float q_descale, float k_descale, float v_descale, void* stream);
+
+/*
  * fa_decode -- attention of one new query row per (b, h) over a whole KV cache,
  * split across workgroups (Flash-Decoding): the cache is cut into nsplit chunks
  * of ceil(Lkv/nsplit) keys; each chunk yields its max, its sum of exponentials

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
-              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_paged"):
+              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_paged", "fa_fwd_fp8"):
         assert n in names
     assert len(names) == len(set(names))
 
@@ -75,6 +75,26 @@ def test_fwd_validation(lib, f32):
     assert fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0, f32=f32) == FA_OK
     assert fwd(lib, N=0, q=0, k=0, v=0, o=0, lse=0, f32=f32) == FA_OK
     assert fwd(lib, H=0, f32=f32) == FA_OK
+
+
+def test_fwd_fp8_validation(lib):
+    def f8(**kw):
+        return lib.fa_fwd_fp8(kw.get("q", A), kw.get("k", Bp), kw.get("v", C), kw.get("o", Dp), kw.get("lse", L),
+                              kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 128), kw.get("causal", 1),
+                              kw.get("scale", 0.088), kw.get("qd", 0.01), kw.get("kd", 0.01), kw.get("vd", 0.01), None)
+    assert f8(d=64) == UNSUPPORTED                                   # FP8 path: d = 128 only
+    assert f8(d=0) == INVALID
+    for bad in (float("nan"), float("inf"), -1.0):
+        assert f8(scale=bad) == INVALID
+        assert f8(qd=bad) == INVALID
+        assert f8(vd=bad) == INVALID
+    assert f8(q=0) == INVALID
+    assert f8(v=C + 4) == INVALID
+    assert f8(lse=L + 1) == INVALID
+    assert f8(o=A) == INVALID                                        # output over q
+    assert f8(o=Bp - 16 * 128) == INVALID                            # bf16 output (4 KiB) running into k
+    assert f8(lse=A + 8 * 128) == INVALID                            # lse inside q
+    assert f8(N=0, q=0, k=0, v=0, o=0, lse=0) == FA_OK
 
 
 def test_decode_validation(lib):
