@@ -17,8 +17,8 @@
 //    score 32 keys; four accumulate one 64-key unit of P V;
 //  * K/V tiles of 128 keys (128 bytes per key) are copied HBM -> LDS with
 //    global_load_lds_dwordx4 into a 4-slot ring; the 16-byte chunks of a key
-//    are XOR-swizzled by bits 1..3 of the key, which keeps both the K row
-//    reads and the transposing V reads free of bank conflicts;
+//    are XOR-swizzled by key bits (K and V differently), which keeps both the
+//    K row reads and the transposing V reads free of bank conflicts;
 //  * P^T for a 64-key unit comes from the two 32-key score accumulators: lane
 //    l's k-slot 16*st + r holds the probability of accumulator st's element r,
 //    so V^T's k-slots are gathered to match with ds_read_b64_tr_b8 (within a
@@ -55,7 +55,14 @@ struct Fp8Tile {
 constexpr int kP8Shift = 6;             // exponent offset of the stored probabilities
 constexpr float kP8Threshold = 2.f;     // reference raise threshold, exp2 units
 
+// K rows are read 16 keys at one logical chunk: bits 1..3 of the key spread
+// them over all eight 16-byte positions (the key's parity picks the other half
+// of the 64 banks).
 __device__ __forceinline__ int swz8(int key) { return (key >> 1) & 7; }
+// A transposing V read of a half-wave touches keys {0..3, 8..11} (+4) at two
+// adjacent chunks; bits 1 and 3 of the key move each key to its own pair of
+// positions, so the 8 keys x 2 chunks cover all 16 bank groups.
+__device__ __forceinline__ int swz8v(int key) { return 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1); }
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -97,9 +104,8 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
       const int v = w * T::IPW + i;
       const int kr = 8 * v + (l >> 3);
       const size_t key = (size_t)min(j * T::BC + kr, N - 1);  // keys past N: any valid row, masked later
-      const int chunk = (l & 7) ^ swz8(kr);
-      global_load_lds16(Kh + key * D + 16 * chunk, kb + v * 1024);
-      global_load_lds16(Vh + key * D + 16 * chunk, vb + v * 1024);
+      global_load_lds16(Kh + key * D + 16 * ((l & 7) ^ swz8(kr)), kb + v * 1024);
+      global_load_lds16(Vh + key * D + 16 * ((l & 7) ^ swz8v(kr)), vb + v * 1024);
     }
   };
 
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     const int t = l & 15, g = l >> 4, e = t >> 1;
     const int key = 8 * (e >> 2) + (e & 3) + 4 * hf;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) v_lane[db] = T::VREG + key * D + 16 * ((2 * db + (g & 1)) ^ swz8(key)) + 8 * (t & 1);
+    for (int db = 0; db < 4; ++db) v_lane[db] = T::VREG + key * D + 16 * ((2 * db + (g & 1)) ^ swz8v(key)) + 8 * (t & 1);
   }
 
   // 64-key unit u lives in tile u / 2, keys 64 * (u % 2) .. of its slot
