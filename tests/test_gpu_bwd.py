@@ -139,3 +139,12 @@ def test_bwd_guard_bands_untouched():
     torch.cuda.synchronize()
     for b in bufs:
         assert (b[:4096] == 7).all() and (b[4096 + n:] == 7).all()
+
+
+def test_bwd_workload_8k_causal_k2_two_heads():
+    """The backward as the benchmark times it (the 8K causal prefill inputs, K doubled, the same
+    seeded dO): two whole heads of dQ, dK and dV against the oracle (dK and dV need every query)."""
+    w = si.WORKLOADS["bf16_h32_n8192_d128_causal_k2"]
+    q, k, v = (si.tensor_full(w, t) for t in ("q", "k", "v"))
+    do = si.upstream_grad(w.wid, w.B, w.H, w.N, w.d, "bf16")
+    print(bwd_case(q, k, v, do, True, w.scale, heads=[(0, 0), (0, 31)]))
