@@ -98,3 +98,17 @@ def test_deterministic():
     a = fa.decode(qd, kd, vd, nsplit=64)
     b = fa.decode(qd, kd, vd, nsplit=64)
     assert torch.equal(a, b)
+
+
+def test_shutdown_then_decode_again():
+    """fa_shutdown frees the library's decode workspaces; the next decode allocates afresh and
+    gives the same result, twice over."""
+    got, ref, (qd, kd, vd) = _decode_case(2, 3, 900, 128, 16, seed=90)
+    assert_close(got, ref, "bf16")
+    first = fa.decode(qd, kd, vd, nsplit=16)
+    for _ in range(2):
+        torch.cuda.synchronize()
+        fa.shutdown()
+        again = fa.decode(qd, kd, vd, nsplit=16)
+        torch.cuda.synchronize()
+        assert torch.equal(first, again)
