@@ -125,16 +125,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 }
 
 // ---- dK, dV: one workgroup per 128 keys of one head ----
-template <int D, bool CAUSAL>
+// Causality is a run-time flag here (uniform branches): the causal and
+// non-causal cases then share one register allocation, which fits without
+// spills.
+template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                           const float* __restrict__ lse2, const float* __restrict__ Dsum,
                                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
-                                                          int Npad, float scale, float c2, int BH) {
+                                                          int Npad, float scale, float c2, int BH, int causal_flag) {
+  const bool CAUSAL = causal_flag != 0;
   using T = BwdTile<D>;
   constexpr int SLOT = 2 * T::BYTES + 512;  // Q tile, dO tile, 64 x (LSE2, D) floats
   constexpr int IPW = 2 * T::NCOPY / 4;     // copy instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * SLOT];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,8 +176,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const TileLanes tl(l);
   const int n_qt = (N + BT - 1) / BT;
   const int qt0 = CAUSAL ? k0 / BT : 0;  // earlier query tiles see none of these keys
-  auto copy = [&](int qt, int slot) __attribute__((always_inline)) {
-    const uint32_t base = lds_addr(lds) + slot * SLOT;
+  const int n_t = n_qt > qt0 ? n_qt - qt0 : 0;  // query tiles this workgroup visits
+  // ring of three slots: tile t (counted from qt0) sits in slot t % 3
+  auto copy = [&](int t) __attribute__((always_inline)) {
+    const int qt = qt0 + t;
+    const uint32_t base = lds_addr(lds) + (t % 3) * SLOT;
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
       const int v = w * IPW + i;  // 0 .. NCOPY - 1: Q, then dO
@@ -188,61 +195,113 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
     }
   };
 
-  if (qt0 < n_qt) copy(qt0, 0);
-  wait_vmcnt<0>();
-  __syncthreads();
-  for (int qt = qt0; qt < n_qt; ++qt) {
-    const int slot = (qt - qt0) & 1;
-    if (qt + 1 < n_qt) copy(qt + 1, slot ^ 1);
-    const int tQ = slot * SLOT, tdO = tQ + T::BYTES;
+  // 32-query block b: rows (qt0 + b/2) * 64 + 32 * (b % 2) .. + 31, in tile b / 2
+  auto blk_q0 = [&](int b) { return (qt0 + (b >> 1)) * BT + 32 * (b & 1); };
+  auto blk_valid = [&](int b) {
+    const int qb0 = blk_q0(b);
+    return b < 2 * n_t && qb0 < N && (!CAUSAL || qb0 + 31 >= kw0);
+  };
+  auto blk_tile = [](int b) { return ((b >> 1) % 3) * SLOT; };
+  // Row fragments (A operands of S and dP) of block b. Blocks past the end
+  // read an in-range ring slot; the values are never used.
+  auto read_rows = [&](bf16x8(&rq)[T::NC], bf16x8(&rd)[T::NC], int b) __attribute__((always_inline)) {
+    const int tQ = blk_tile(b), h = b & 1;
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+      rq[c] = row_frag(lds, tQ, tl, h, c);
+      rd[c] = row_frag(lds, tQ + T::BYTES, tl, h, c);
+    }
+  };
+  auto score = [&](f32x16& sc, f32x16& dp, const bf16x8(&rq)[T::NC], const bf16x8(&rd)[T::NC])
+                   __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) {
+      sc = mfma32x32x16(rq[c], kT[c], c == 0 ? (f32x16){} : sc);
+      dp = mfma32x32x16(rd[c], vT[c], c == 0 ? (f32x16){} : dp);
+    }
+  };
+  // One block: the scores of block b + 1 go to the matrix cores first (their
+  // row fragments were read one block earlier), the row fragments of block
+  // b + 2 and the transposed fragments of block b are read, then P and dS of
+  // block b are formed while those MFMAs run, and dV, dK accumulate.
+  // Lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf.
+  auto block = [&](f32x16& sc, f32x16& dp, f32x16& sc_n, f32x16& dp_n, const bf16x8(&rq_n)[T::NC],
+                   const bf16x8(&rd_n)[T::NC], bf16x8(&rq_f)[T::NC], bf16x8(&rd_f)[T::NC], int b)
+                   __attribute__((always_inline)) {
+    const bool cur = blk_valid(b);
+    if (blk_valid(b + 1)) score(sc_n, dp_n, rq_n, rd_n);
+    read_rows(rq_f, rd_f, b + 2);
+    if (!cur) return;
+    const int tQ = blk_tile(b), tdO = tQ + T::BYTES, h = b & 1;
+    bf16x8 tq[T::NDB], td[T::NDB];  // transposed fragments of one 16-query half (kc)
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db) {
+      td[db] = tr_frag(lds, tdO, tl, h, 0, db);
+      tq[db] = tr_frag(lds, tQ, tl, h, 0, db);
+    }
     const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
+    const int qb0 = blk_q0(b);
+    const bool need_mask = (qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31);
+    bf16x8 pb[2], sb[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int qb0 = qt * BT + 32 * h;  // first query of the 32-row block
-      if (qb0 >= N || (CAUSAL && qb0 + 31 < kw0)) continue;
-      f32x16 sc = (f32x16){}, dp = (f32x16){};
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 L4 = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
+      const f32x4 D4 = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
 #pragma unroll
-      for (int c = 0; c < T::NC; ++c) {
-        sc = mfma32x32x16(row_frag(lds, tQ, tl, h, c), kT[c], sc);
-        dp = mfma32x32x16(row_frag(lds, tdO, tl, h, c), vT[c], dp);
-      }
-      // lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf
-      const bool need_mask = (qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31);
-      bf16x8 pb[2], sb[2];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 L4 = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
-        const f32x4 D4 = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r = 4 * rb + e;
-          float p0 = fast_exp2(fmaf(sc[r], c2, -L4[e]));
-          float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L4[e + 1]));
-          if (need_mask) {
-            const int q = qb0 + 8 * rb + 4 * hf + e, key = kw0 + lq;
-            p0 = (q < N && (!CAUSAL || key <= q)) ? p0 : 0.f;
-            p1 = (q + 1 < N && (!CAUSAL || key <= q + 1)) ? p1 : 0.f;
-          }
-          const float d0 = p0 * (dp[r] - D4[e]), d1 = p1 * (dp[r + 1] - D4[e + 1]);
-          const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
-          pb[r >> 3][r & 7] = pp[0];
-          pb[r >> 3][(r & 7) + 1] = pp[1];
-          sb[r >> 3][r & 7] = ss[0];
-          sb[r >> 3][(r & 7) + 1] = ss[1];
+      for (int e = 0; e < 4; e += 2) {
+        const int r = 4 * rb + e;
+        float p0 = fast_exp2(fmaf(sc[r], c2, -L4[e]));
+        float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L4[e + 1]));
+        if (need_mask) {
+          const int q = qb0 + 8 * rb + 4 * hf + e, key = kw0 + lq;
+          p0 = (q < N && (!CAUSAL || key <= q)) ? p0 : 0.f;
+          p1 = (q + 1 < N && (!CAUSAL || key <= q + 1)) ? p1 : 0.f;
         }
+        const float d0 = p0 * (dp[r] - D4[e]), d1 = p1 * (dp[r + 1] - D4[e + 1]);
+        const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
+        pb[r >> 3][r & 7] = pp[0];
+        pb[r >> 3][(r & 7) + 1] = pp[1];
+        sb[r >> 3][r & 7] = ss[0];
+        sb[r >> 3][(r & 7) + 1] = ss[1];
       }
-      // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
-      // the lane's queries), B = dO / Q through the transposing read
+    }
+    // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
+    // the lane's queries), B = dO / Q through the transposing read
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
+    for (int kc = 0; kc < 2; ++kc) {
+      if (kc == 1) {
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) {
-          dv[db] = mfma32x32x16(pb[kc], tr_frag(lds, tdO, tl, h, kc, db), dv[db]);
-          dk[db] = mfma32x32x16(sb[kc], tr_frag(lds, tQ, tl, h, kc, db), dk[db]);
+          td[db] = tr_frag(lds, tdO, tl, h, 1, db);
+          tq[db] = tr_frag(lds, tQ, tl, h, 1, db);
         }
+      }
+#pragma unroll
+      for (int db = 0; db < T::NDB; ++db) {
+        dv[db] = mfma32x32x16(pb[kc], td[db], dv[db]);
+        dk[db] = mfma32x32x16(sb[kc], tq[db], dk[db]);
+      }
     }
+  };
+
+  // Tile t + 1 is resident while tile t is processed (block 2t + 1 reads the
+  // rows of the first block of tile t + 1); tile t + 2 is copied during tile
+  // t into the slot of tile t - 1 and published by the barrier that ends t.
+  if (n_t > 0) copy(0);
+  if (n_t > 1) copy(1);
+  wait_vmcnt<0>();
+  __syncthreads();
+  f32x16 scA, dpA, scB, dpB;
+  bf16x8 rqA[T::NC], rdA[T::NC], rqB[T::NC], rdB[T::NC];
+  read_rows(rqA, rdA, 0);
+  if (blk_valid(0)) score(scA, dpA, rqA, rdA);
+  read_rows(rqB, rdB, 1);
+  for (int t = 0; t < n_t; ++t) {
+    if (t + 2 < n_t) copy(t + 2);
+    block(scA, dpA, scB, dpB, rqB, rdB, rqA, rdA, 2 * t);
+    block(scB, dpB, scA, dpA, rqA, rdA, rqB, rdB, 2 * t + 1);
     wait_vmcnt<0>();
-    __syncthreads();  // tile qt + 1 resident; every wave done with tile qt
+    __syncthreads();
   }
 
   // lane l holds head dim 32*db + lq of keys kw0 + (r%4) + 8(r/4) + 4hf
@@ -393,8 +452,9 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   if (e != hipSuccess) return e;
 
   dim3 g1((unsigned)(((N + 127) / 128) * BH)), b1(256);
-  void* a1[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dkp, &dvp, &N, &Npad, &scale, &c2, (void*)&BH};
-  e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<D, CAUSAL>, g1, b1, a1, 0, s);
+  int causal_flag = CAUSAL ? 1 : 0;
+  void* a1[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dkp, &dvp, &N, &Npad, &scale, &c2, (void*)&BH, &causal_flag};
+  e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<D>, g1, b1, a1, 0, s);
   if (e != hipSuccess) return e;
 
   int n_qt = (N + 255) / 256;
