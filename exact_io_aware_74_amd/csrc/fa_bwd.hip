@@ -20,13 +20,16 @@
 //    S = Q K^T and dP = dO V^T (lane l holds key l % 32 and 16 queries), forms
 //    P and dS in registers and accumulates dV += P^T dO and dK += dS^T Q, the
 //    P^T / dS^T operands coming straight from those registers and dO / Q
-//    through the transposing LDS read;
+//    through the transposing LDS read. With a single wave per SIMD the
+//    kernel pipelines itself: the S / dP MFMAs of the next block (from row
+//    fragments read a block ahead) run while this block's P and dS are
+//    formed;
 //  * bwd_dq: one workgroup per 256 queries (8 waves x 32 rows), laid out like
 //    the forward: S^T = K Q^T and dP^T = V dO^T with Q / dO in VGPRs, then
 //    dQ^T += K^T dS^T with K^T from the transposing read. No atomics: dQ is
 //    owned by one wave, so results are deterministic.
-// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into two slots
-// (one barrier per tile), row-major by 64-dim octets with the 16-byte chunks
+// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into a ring (three
+// slots for dK / dV, two for dQ; one barrier per tile), row-major by 64-dim octets with the 16-byte chunks
 // XOR-swizzled per row by one function that keeps both the row-fragment reads
 // (16 rows, one chunk) and the transposing reads (4 rows x 4 chunks) free of
 // bank conflicts.
