@@ -1,7 +1,7 @@
 // C ABI of the attention library (declared in include/fa.h): argument
 // validation, kernel dispatch and the decode workspace. Every check runs
 // before anything is enqueued, so a call that fails has no device effects.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <climits>
 #include <cmath>

@@ -1,7 +1,7 @@
 // Host-side launchers of the attention kernels (internal to the library; the
 // public surface is the C ABI in fa.h). Arguments are assumed validated.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 
 namespace fa {
