@@ -310,6 +310,9 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
       mx[qb] = -INFINITY;
     }
     constexpr int EARLY = 3 * NPAIR / 4;  // pairs computed under the score MFMAs
+    // The score MFMAs run at raised wave priority: when both waves of a SIMD
+    // can issue, the one feeding the matrix core goes first (measured 1-2%).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
 #pragma unroll
@@ -320,6 +323,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
         prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
       if (c < T::NDB) vf[0][c] = load_v(v_slot, h, 0, c);  // the 16-key chunk kc = 1 follows below
     }
+    __builtin_amdgcn_s_setprio(0);
     constexpr int PER = 16 / (2 * T::NDB);  // max elements per query block per head-dim block
 #pragma unroll
     for (int i = 0; i < 2 * T::NDB; ++i) {
