@@ -78,7 +78,16 @@ def cpu_baseline(w, target_s: float):
         assert np.isfinite(O).all()
         flops += oracle.attention_flops(1, 1, w.N, w.d, w.causal)
         heads += 1
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"{heads} of {w.H} heads of the N=8192 d=128 causal prefill (all rows), fp64 numpy, "
                       f"{elapsed:.1f} s"}
 
