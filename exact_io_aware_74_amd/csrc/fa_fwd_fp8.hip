@@ -189,12 +189,16 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
 
   // One unit: P V for unit u from its scores `cur`, while the scores of unit
-  // u + 1 are computed into `nxt` and the K rows of unit u + 2 are read.
+  // u + 1 are computed into `nxt` and the K rows of unit u + 2 are read. That
+  // read is unconditional: past the last unit it reads a ring slot (in bounds,
+  // possibly being refilled) into fragments nobody uses, and it keeps the
+  // fragments in one set of registers (a conditional read costs a 32-register
+  // copy per unit).
   auto step = [&](f32x16(&cur)[2], f32x16(&nxt)[2], int u) __attribute__((always_inline)) {
     if (u >= n_u) return;
     if (u + 1 < n_u) {
       qk(nxt, kf);
-      if (u + 2 < n_u) read_k(kf, u + 2);
+      read_k(kf, u + 2);
     }
     if ((64 * u + 64 > N) || (CAUSAL && 64 * u + 63 > wq0)) {
 #pragma unroll
