@@ -43,6 +43,7 @@ namespace {
 
 constexpr int BT = 64;  // rows per LDS tile
 
+
 __device__ __forceinline__ int bswz(int row) { return 4 * ((row >> 1) & 1) + ((row >> 2) & 3); }
 
 template <int D>
@@ -200,10 +201,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
 
   // 32-query block b: rows (qt0 + b/2) * 64 + 32 * (b % 2) .. + 31, in tile b / 2
   auto blk_q0 = [&](int b) { return (qt0 + (b >> 1)) * BT + 32 * (b & 1); };
-  auto blk_valid = [&](int b) {
-    const int qb0 = blk_q0(b);
-    return b < 2 * n_t && qb0 < N && (!CAUSAL || qb0 + 31 >= kw0);
-  };
   auto blk_tile = [](int b) { return ((b >> 1) % 3) * SLOT; };
   // Row fragments (A operands of S and dP) of block b. Blocks past the end
   // read an in-range ring slot; the values are never used.
@@ -223,51 +220,80 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
       dp = mfma32x32x16(rd[c], vT[c], c == 0 ? (f32x16){} : dp);
     }
   };
-  // One block: the scores of block b + 1 go to the matrix cores first (their
-  // row fragments were read one block earlier), the row fragments of block
-  // b + 2 and the transposed fragments of block b are read, then P and dS of
-  // block b are formed while those MFMAs run, and dV, dK accumulate.
+  // One block b. With one wave per SIMD the wave issues in order, so the
+  // matrix cores only stay busy if MFMAs and arithmetic alternate in its
+  // instruction stream. The block is one straight-line region (masked blocks
+  // first set their hidden scores to -inf in a uniform branch), laid out as:
+  // the LSE / D values of block b and the transposed fragments of its first
+  // 16 queries are read (LDS answers in issue order, so these come first);
+  // the score MFMAs of block b + 1 alternate with forming P and dS of block
+  // b (the row fragments of b + 1 were read one block earlier; past the last
+  // block they score an in-range ring slot nobody uses); the row fragments
+  // of block b + 2 are read into the registers those MFMAs consumed; dV and
+  // dK accumulate.
   // Lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf.
   auto block = [&](f32x16& sc, f32x16& dp, f32x16& sc_n, f32x16& dp_n, const bf16x8(&rq_n)[T::NC],
                    const bf16x8(&rd_n)[T::NC], bf16x8(&rq_f)[T::NC], bf16x8(&rd_f)[T::NC], int b)
                    __attribute__((always_inline)) {
-    const bool cur = blk_valid(b);
-    if (blk_valid(b + 1)) score(sc_n, dp_n, rq_n, rd_n);
-    read_rows(rq_f, rd_f, b + 2);
-    if (!cur) return;
-    const int tQ = blk_tile(b), tdO = tQ + T::BYTES, h = b & 1;
-    bf16x8 tq[T::NDB], td[T::NDB];  // transposed fragments of one 16-query half (kc)
-#pragma unroll
-    for (int db = 0; db < T::NDB; ++db) {
-      td[db] = tr_frag(lds, tdO, tl, h, 0, db);
-      tq[db] = tr_frag(lds, tQ, tl, h, 0, db);
-    }
-    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
+    // A block before the diagonal (causal) or past the last row has every
+    // score masked, so its P and dS are exactly 0 and it adds nothing.
     const int qb0 = blk_q0(b);
-    const bool need_mask = (qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31);
-    bf16x8 pb[2], sb[2];
+    if ((qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31)) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 L4 = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
-      const f32x4 D4 = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
-#pragma unroll
-      for (int e = 0; e < 4; e += 2) {
-        const int r = 4 * rb + e;
-        float p0 = fast_exp2(fmaf(sc[r], c2, -L4[e]));
-        float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L4[e + 1]));
-        if (need_mask) {
-          const int q = qb0 + 8 * rb + 4 * hf + e, key = kw0 + lq;
-          p0 = (q < N && (!CAUSAL || key <= q)) ? p0 : 0.f;
-          p1 = (q + 1 < N && (!CAUSAL || key <= q + 1)) ? p1 : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
+        if (!(q < N && (!CAUSAL || key <= q))) {
+          sc[r] = -INFINITY;  // P = 0
+          dp[r] = 0.f;        // dS = 0 * (0 - D) = 0 whatever the row data holds
         }
-        const float d0 = p0 * (dp[r] - D4[e]), d1 = p1 * (dp[r + 1] - D4[e + 1]);
-        const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
-        pb[r >> 3][r & 7] = pp[0];
-        pb[r >> 3][(r & 7) + 1] = pp[1];
-        sb[r >> 3][r & 7] = ss[0];
-        sb[r >> 3][(r & 7) + 1] = ss[1];
       }
     }
+    const int tQ = blk_tile(b), tdO = tQ + T::BYTES, h = b & 1;
+    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
+    auto read_stats = [&](f32x4& L, f32x4& Dv, int rb) __attribute__((always_inline)) {
+      L = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
+      Dv = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
+    };
+    // Eight groups: the two score MFMAs of head-dim chunk j for block b + 1,
+    // then P and dS of elements 2j, 2j + 1 of block b. The LSE / D values are
+    // read one group pair ahead and the transposed fragments of the first 16
+    // queries during the second half; the fences keep this order and the
+    // register pressure of source order.
+    f32x4 L4[2], D4[2];
+    bf16x8 tq[T::NDB], td[T::NDB];  // transposed fragments of one 16-query half (kc)
+    bf16x8 pb[2], sb[2];
+    read_stats(L4[0], D4[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rb = j >> 1, e = 2 * (j & 1), r = 2 * j;
+      if ((j & 1) == 0 && rb < 3) read_stats(L4[(rb + 1) & 1], D4[(rb + 1) & 1], rb + 1);
+      if (j >= 8 - T::NDB) {
+        const int db = j - (8 - T::NDB);
+        td[db] = tr_frag(lds, tdO, tl, h, 0, db);
+        tq[db] = tr_frag(lds, tQ, tl, h, 0, db);
+      }
+      if (j < T::NC) {
+        sc_n = mfma32x32x16(rq_n[j], kT[j], j == 0 ? (f32x16){} : sc_n);
+        dp_n = mfma32x32x16(rd_n[j], vT[j], j == 0 ? (f32x16){} : dp_n);
+      }
+      const f32x4 L = L4[rb & 1], Dv = D4[rb & 1];
+      const float p0 = fast_exp2(fmaf(sc[r], c2, -L[e]));
+      const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
+      const float d0 = p0 * (dp[r] - Dv[e]), d1 = p1 * (dp[r + 1] - Dv[e + 1]);
+      const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
+      pb[r >> 3][r & 7] = pp[0];
+      pb[r >> 3][(r & 7) + 1] = pp[1];
+      sb[r >> 3][r & 7] = ss[0];
+      sb[r >> 3][(r & 7) + 1] = ss[1];
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 8; c < T::NC; ++c) {  // head dims past 128 (none at d = 128)
+      sc_n = mfma32x32x16(rq_n[c], kT[c], sc_n);
+      dp_n = mfma32x32x16(rd_n[c], vT[c], dp_n);
+    }
+    read_rows(rq_f, rd_f, b + 2);
     // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
     // the lane's queries), B = dO / Q through the transposing read
 #pragma unroll
@@ -297,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   f32x16 scA, dpA, scB, dpB;
   bf16x8 rqA[T::NC], rdA[T::NC], rqB[T::NC], rdB[T::NC];
   read_rows(rqA, rdA, 0);
-  if (blk_valid(0)) score(scA, dpA, rqA, rdA);
+  score(scA, dpA, rqA, rdA);
   read_rows(rqB, rdB, 1);
   for (int t = 0; t < n_t; ++t) {
     if (t + 2 < n_t) copy(t + 2);
