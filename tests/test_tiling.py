@@ -93,7 +93,9 @@ def fwd_fp8_model(N, causal):
 
 def bwd_dkdv_model(N, causal):
     """bwd_dkdv_kernel: 128-key workgroups, 32 keys per wave, 32-query blocks of 64-row tiles
-    from query tile k0 / 64 on (causal)."""
+    from query tile k0 / 64 on (causal). Every block of the visited tiles is computed; a block
+    with no visible pair (before the diagonal, or past the last row) must take the masked path,
+    which zeroes all of its probabilities."""
     BT = 64
     cover = np.zeros((N, N), dtype=np.int64)
     n_qt = math.ceil(N / BT)
@@ -110,10 +112,10 @@ def bwd_dkdv_model(N, causal):
                 qb0 = (qt0 + b // 2) * BT + 32 * (b % 2)
                 valid = qb0 < N and (not causal or qb0 + 31 >= kw0)
                 vis = visible(N, causal)[qb0:min(qb0 + 32, N), c0:c1] if qb0 < N else np.zeros((0, 0), bool)
-                if not valid:
-                    assert not vis.any()
-                    continue
                 need_mask = (qb0 + 32 > N) or (causal and qb0 < kw0 + 31)
+                if not valid:
+                    assert not vis.any() and need_mask
+                    continue
                 if not need_mask:
                     assert vis.all()
                 cover[qb0:min(qb0 + 32, N), c0:c1] += vis
