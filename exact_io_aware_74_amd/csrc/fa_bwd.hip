@@ -421,18 +421,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
         sT = mfma32x32x16(row_frag(lds, tK, tl, h, c), qT[c], sT);
         dpT = mfma32x32x16(row_frag(lds, tV, tl, h, c), doT[c], dpT);
       }
-      // lane: query qrow; element r: key 32t + (r%4) + 8(r/4) + 4hf
-      const bool need_mask = (32 * t + 32 > N) || (CAUSAL && 32 * t + 31 > wq0);
+      // lane: query qrow; element r: key 32t + (r%4) + 8(r/4) + 4hf. Hidden
+      // scores become -inf (P = 0) and their dP 0 (dS = 0) in one uniform
+      // branch, so the probability code below is straight-line.
+      if ((32 * t + 32 > N) || (CAUSAL && 32 * t + 31 > wq0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
+          if (!(key < N && (!CAUSAL || key <= qrow))) {
+            sT[r] = -INFINITY;
+            dpT[r] = 0.f;
+          }
+        }
+      }
       bf16x8 sb[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        float p0 = fast_exp2(fmaf(sT[r], c2, -lq2));
-        float p1 = fast_exp2(fmaf(sT[r + 1], c2, -lq2));
-        if (need_mask) {
-          const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
-          p0 = (key < N && (!CAUSAL || key <= qrow)) ? p0 : 0.f;
-          p1 = (key + 1 < N && (!CAUSAL || key + 1 <= qrow)) ? p1 : 0.f;
-        }
+        const float p0 = fast_exp2(fmaf(sT[r], c2, -lq2));
+        const float p1 = fast_exp2(fmaf(sT[r + 1], c2, -lq2));
         const bf16x2 ss = to_bf16x2(p0 * (dpT[r] - dq_d), p1 * (dpT[r + 1] - dq_d));
         sb[r >> 3][r & 7] = ss[0];
         sb[r >> 3][(r & 7) + 1] = ss[1];
