@@ -183,7 +183,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 
   f32x16 sA[2], sB[2];
   f32x16 oacc[4];
-  i32x8 kf[2][2];
+  i32x8 kf[2][2], pb = {};
   float m = -INFINITY, lsum = 0.f;
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
@@ -227,7 +227,6 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     }
     const float mc = m * c2 - (float)kP8Shift;
     float ps = 0.f;
-    i32x8 pb;
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
       const int st = wd >> 2, r0 = 4 * (wd & 3);
@@ -237,7 +236,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
         p[i] = fast_exp2(fmaf(cur[st][r0 + i], c2, -mc));
         ps += p[i];
       }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the conversion writes one half of the word and keeps the other; the
+      // previous word stands in for it (overwritten next), so no zero is set
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[wd], false);
       word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
       pb[wd] = word;
     }
