@@ -12,9 +12,11 @@ Prints one JSON line: `value` is the prefill's attention-forward throughput
 fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
 throughput on a bounded sample of the prefill workload in `cpu_baseline`.
 After the timed steps, the same decode over a paged cache (`paged_decode`),
-the backward pass on the prefill workload (`backward`), the FP8 forward on the
-prefill workload (`fp8_prefill`) and a 128K-token prefill (`long_prefill`)
-are timed on their own and reported apart from `value`.
+the backward pass on the prefill workload (`backward`), the other configurations
+of the plan (`reported_configs`: fp32 N=256, bf16 N=1024 d=64, 16K, and the
+three-kernel ablation), the FP8 forward on the prefill workload (`fp8_prefill`)
+and a 128K-token prefill (`long_prefill`) are timed on their own and reported
+apart from `value`.
 """
 from __future__ import annotations
 
@@ -32,6 +34,7 @@ METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak) at N=8K d=128; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the published 2.5 PFLOP/s dense)
 PEAK_HBM_GBPS = 8000.0       # published HBM3E bandwidth
 PEAK_FP8_TFLOPS = 5033.2     # dense FP8 MFMA: twice the bf16 rate (the published 5.0 PFLOP/s)
+PEAK_FP32_TFLOPS = 157.3     # published fp32 rate (the fp32 forward is a VALU kernel; reported for information)
 PREFILL = "bf16_h32_n8192_d128_causal_k2"
 DECODE = "decode_b16h32_l32768_d128"
 LONG = "bf16_b4h32_n131072_d128_causal"
@@ -222,6 +225,84 @@ def long_prefill_leg(fa, torch, si, steps):
             "workload": "prefill B=4 H=32 N=131072 d=128 bf16 causal, N(0,1) inputs from a seeded device generator"}
 
 
+def reported_configs_leg(fa, torch, si, wp, q, k, v, steps):
+    """The configurations reported beside the gated ones, each timed on its own with
+    HIP events on the launch stream: the fp32 forward at N=256 d=64, the bf16 forward
+    at B=4 H=16 N=1024 d=64 causal, the bf16 forward at the 16K causal workload
+    (inputs N(0,1) from a seeded device generator), and the three-kernel ablation
+    (S and P through HBM) at N=1024 and at the prefill workload next to the fused kernel."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn()
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+        return sum(ms) / len(ms), min(ms)
+
+    def pairs(w):
+        return w.B * w.H * (w.N * (w.N + 1) // 2 if w.causal else w.N * w.N)
+
+    def entry(w, flops, avg, mn, peak, kernel):
+        tf = flops / (avg * 1e-3) / 1e12
+        return {"value": round(tf, 3), "unit": "TFLOP/s", "frac_of_peak": round(tf / peak, 4), "peak": peak,
+                "ms": round(avg, 4), "ms_min": round(mn, 4), "flop_per_call": flops, "kernel": kernel,
+                "workload": f"B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}{' causal' if w.causal else ''}"}
+
+    def to_bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    res = {}
+    w1 = si.WORKLOADS["f32_n256_d64"]
+    q1, k1, v1 = (torch.from_numpy(si.tensor_full(w1, t)).cuda() for t in ("q", "k", "v"))
+    avg, mn = timed(lambda: fa.fwd(q1, k1, v1, causal=w1.causal, scale=w1.scale), 5 * steps)
+    res["f32_n256_d64"] = entry(w1, 4 * w1.d * pairs(w1), avg, mn, PEAK_FP32_TFLOPS, "fwd_f32_kernel")
+
+    w2 = si.WORKLOADS["bf16_b4h16_n1024_d64_causal"]
+    q2, k2, v2 = (to_bf16(si.tensor_full(w2, t)) for t in ("q", "k", "v"))
+    avg, mn = timed(lambda: fa.fwd(q2, k2, v2, causal=True, scale=w2.scale), 5 * steps)
+    res["bf16_b4h16_n1024_d64_causal"] = entry(w2, 4 * w2.d * pairs(w2), avg, mn, PEAK_BF16_TFLOPS,
+                                               "fwd_bf16_kernel<64, causal>")
+    ws2 = torch.empty(fa.naive_workspace_bytes(w2.B, w2.H, w2.N) // 4, dtype=torch.float32, device="cuda")
+    avg_n, mn_n = timed(lambda: fa.naive_fwd(q2, k2, v2, causal=True, scale=w2.scale, workspace=ws2), steps)
+    e = entry(w2, 4 * w2.d * pairs(w2), avg_n, mn_n, PEAK_BF16_TFLOPS, "naive_* (ablation)")
+    e["fused_speedup"] = round(avg_n / avg, 2)
+    e["score_bytes_per_call"] = 4 * w2.B * w2.H * w2.N * w2.N * 4   # S written, read, P written, read (fp32)
+    res["ablation_bf16_b4h16_n1024_d64_causal"] = e
+    del q2, k2, v2, ws2
+
+    w4 = si.WORKLOADS["bf16_h32_n16384_d128_causal"]
+    gen = torch.Generator(device="cuda").manual_seed(w4.wid)
+    shape = (w4.B, w4.H, w4.N, w4.d)
+    q4, k4, v4 = (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+                  for _ in range(3))
+    o4 = torch.empty_like(q4)
+    lse4 = torch.empty(shape[:3], dtype=torch.float32, device="cuda")
+    avg, mn = timed(lambda: fa.fwd(q4, k4, v4, causal=True, scale=w4.scale, out=o4, lse=lse4), steps)
+    assert torch.isfinite(lse4).all().item()
+    res["bf16_h32_n16384_d128_causal"] = entry(w4, 4 * w4.d * pairs(w4), avg, mn, PEAK_BF16_TFLOPS,
+                                               "fwd_bf16_kernel<128, causal>")
+    del q4, k4, v4, o4, lse4
+
+    avg_f, _ = timed(lambda: fa.fwd(q, k, v, causal=True, scale=wp.scale), steps)
+    ws3 = torch.empty(fa.naive_workspace_bytes(wp.B, wp.H, wp.N) // 4, dtype=torch.float32, device="cuda")
+    avg_n, mn_n = timed(lambda: fa.naive_fwd(q, k, v, causal=True, scale=wp.scale, workspace=ws3), max(2, steps // 2))
+    e = entry(wp, 4 * wp.d * pairs(wp), avg_n, mn_n, PEAK_BF16_TFLOPS, "naive_* (ablation)")
+    e["fused_speedup"] = round(avg_n / avg_f, 2)
+    e["score_bytes_per_call"] = 4 * wp.B * wp.H * wp.N * wp.N * 4
+    e["workload"] += " (K x2: the prefill workload)"
+    res["ablation_bf16_h32_n8192_d128_causal_k2"] = e
+    del ws3
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +318,9 @@ def main():
                     help="timed calls of the FP8 forward on the prefill workload (reported apart; 0 disables it)")
     ap.add_argument("--long-steps", type=int, default=3,
                     help="timed calls of the 128K-token prefill (reported apart from the step; 0 disables it)")
+    ap.add_argument("--report-steps", type=int, default=10,
+                    help="timed calls per reported configuration (N=256 fp32, N=1024 d=64, 16K, the ablation; "
+                         "reported apart; 0 disables them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
     args = ap.parse_args()
@@ -348,6 +432,8 @@ def main():
         rec["paged_decode"] = paged_decode_leg(fa, torch, si, wd, dq, dk, dv, args.paged_steps)
     if args.bwd_steps > 0:
         rec["backward"] = backward_leg(fa, torch, si, wp, q, k, v, o, lse, args.bwd_steps)
+    if args.report_steps > 0:
+        rec["reported_configs"] = reported_configs_leg(fa, torch, si, wp, q, k, v, args.report_steps)
     del q, k, v, dq, dk, dv, o, do
     if args.fp8_steps > 0:
         rec["fp8_prefill"] = fp8_prefill_leg(fa, torch, si, wp, args.fp8_steps)
