@@ -22,17 +22,18 @@
 //    P^T / dS^T operands coming straight from those registers and dO / Q
 //    through the transposing LDS read. With a single wave per SIMD the
 //    kernel pipelines itself: the S / dP MFMAs of the next block (from row
-//    fragments read a block ahead) run while this block's P and dS are
-//    formed;
+//    fragments read a block ahead) alternate with forming this block's P and
+//    dS in the wave's instruction stream (fenced groups), and masked scores
+//    are set to -inf up front so that code is straight-line;
 //  * bwd_dq: one workgroup per 256 queries (8 waves x 32 rows), laid out like
 //    the forward: S^T = K Q^T and dP^T = V dO^T with Q / dO in VGPRs, then
 //    dQ^T += K^T dS^T with K^T from the transposing read. No atomics: dQ is
 //    owned by one wave, so results are deterministic.
 // Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into a ring (three
-// slots for dK / dV, two for dQ; one barrier per tile), row-major by 64-dim octets with the 16-byte chunks
-// XOR-swizzled per row by one function that keeps both the row-fragment reads
-// (16 rows, one chunk) and the transposing reads (4 rows x 4 chunks) free of
-// bank conflicts.
+// slots for dK / dV, two for dQ; one barrier per tile), row-major by 64-dim
+// octets with the 16-byte chunks XOR-swizzled per row by one function that
+// keeps both the row-fragment reads (16 rows, one chunk) and the transposing
+// reads (4 rows x 4 chunks) free of bank conflicts.
 #include <float.h>
 
 #include "fa_device.h"
