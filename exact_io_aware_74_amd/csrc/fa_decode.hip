@@ -250,9 +250,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restri
   const int bh = blockIdx.x, t = threadIdx.x;
   const float* ml = ws + (size_t)bh * nsplit * 2;
   const float* os = ws + (size_t)BH * nsplit * 2 + (size_t)bh * nsplit * D;
+  // unrolled so that a batch of independent loads is in flight at a time
+  // (one load per iteration would pay the memory latency nsplit times)
   float M = -FLT_MAX;
+#pragma unroll 16
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
   float L = 0.f, acc = 0.f;
+#pragma unroll 16
   for (int s = 0; s < nsplit; ++s) {
     const float wgt = fast_exp2((ml[2 * s] - M) * c2);
     L = fmaf(wgt, ml[2 * s + 1], L);
