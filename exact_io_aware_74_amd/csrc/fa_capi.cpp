@@ -46,7 +46,12 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, const 
   const size_t bytes = (size_t)bh * (size_t)N * (size_t)d * elem;
   if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes))
     return FA_ERR_INVALID_ARG;
-  if (lse && overlaps(lse, (size_t)bh * N * 4, o, bytes)) return FA_ERR_INVALID_ARG;
+  if (lse) {
+    const size_t lbytes = (size_t)bh * N * 4;
+    if (overlaps(lse, lbytes, o, bytes) || overlaps(lse, lbytes, q, bytes) || overlaps(lse, lbytes, k, bytes) ||
+        overlaps(lse, lbytes, v, bytes))
+      return FA_ERR_INVALID_ARG;
+  }
   return FA_OK;
 }
 
@@ -78,9 +83,6 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
-// The decode partials buffer of (current device, stream), grown to `need`
-// bytes if smaller. Growing synchronises the stream first: earlier decodes on
-// it may still read the old buffer.
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                int causal, float scale, float q_descale, float k_descale, float v_descale, void* stream) {
   if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARG;
@@ -104,6 +106,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+// The decode partials buffer of (current device, stream), grown to `need`
+// bytes if smaller. Growing synchronises the stream first: earlier decodes on
+// it may still read the old buffer.
 static int decode_workspace(void* stream, size_t need, float** ws) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);

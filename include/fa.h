@@ -59,7 +59,8 @@ enum fa_status {
  *
  *   q, k, v  const bf16 [B,H,N,d]; o: bf16 [B,H,N,d] (may not alias q, k, v)
  *   lse      float32 [B,H,N], natural-log log-sum-exp of each row's scaled
- *            logits over its visible keys; NULL = not written
+ *            logits over its visible keys; NULL = not written; may not
+ *            overlap q, k, v or o
  *   causal   nonzero: key j is visible to query i iff j <= i
  *   scale    multiplier of the logits; must be finite and >= 0
  *   d        64 or 128 (else FA_ERR_UNSUPPORTED)

@@ -70,6 +70,8 @@ def test_fwd_validation(lib, f32):
     assert fwd(lib, scale=-0.5, f32=f32) == INVALID
     assert fwd(lib, o=A, f32=f32) == INVALID                        # output aliases q
     assert fwd(lib, o=A + 256, f32=f32) == INVALID                  # output overlaps q
+    assert fwd(lib, lse=Bp + 64, f32=f32) == INVALID                # lse inside k
+    assert fwd(lib, lse=Dp, f32=f32) == INVALID                     # lse on the output
     assert fwd(lib, B=1 << 20, H=1 << 12, N=1 << 12, f32=f32) == INVALID   # grid overflow
     # empty problems succeed without touching anything (null pointers allowed)
     assert fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0, f32=f32) == FA_OK
