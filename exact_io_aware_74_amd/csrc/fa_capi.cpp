@@ -88,7 +88,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (B < 0 || H < 0 || N < 0 || d <= 0) return FA_ERR_INVALID_ARG;
   for (float x : {scale, q_descale, k_descale, v_descale})
     if (!std::isfinite(x) || x < 0.f) return FA_ERR_INVALID_ARG;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || N == 0) return FA_OK;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
@@ -101,7 +101,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (lse && (overlaps(lse, (size_t)bh * N * 4, o, out_bytes) || overlaps(lse, (size_t)bh * N * 4, q, in_bytes) ||
               overlaps(lse, (size_t)bh * N * 4, k, in_bytes) || overlaps(lse, (size_t)bh * N * 4, v, in_bytes)))
     return FA_ERR_INVALID_ARG;
-  const hipError_t e = fa::launch_fwd_fp8(q, k, v, o, lse, B, H, N, causal != 0, scale, q_descale, k_descale,
+  const hipError_t e = fa::launch_fwd_fp8(q, k, v, o, lse, B, H, N, d, causal != 0, scale, q_descale, k_descale,
                                           v_descale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }

@@ -9,7 +9,8 @@
 // FA-3). The pages give no scaling convention; this kernel takes one float
 // descale factor per tensor, so the logical inputs are q_descale * Q8, etc.
 //
-// Mapping (d = 128 only):
+// Mapping (d = 128; d = 64 is the same with half the chunks per key row, one
+// score MFMA per 32 keys and two 32-dim blocks of O^T):
 //  * eight waves x 32 query rows per workgroup; S^T = K Q^T and O^T += V^T P^T
 //    on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales), 64 contraction slots
 //    per instruction: lane l holds row l % 32 and k-slots 32*(l/32) .. +31 of
@@ -39,8 +40,13 @@ namespace fa {
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 
+template <int HD>
 struct Fp8Tile {
-  static constexpr int D = 128;        // head dimension = bytes per key row
+  static constexpr int D = HD;         // head dimension = bytes per key row (64 or 128)
+  static constexpr int NCH = D / 16;   // 16-byte chunks per key row
+  static constexpr int KPI = 1024 / D; // keys per 1 KB copy instruction
+  static constexpr int NQ = D / 64;    // score MFMAs per 32-key sub-tile (64 contraction slots each)
+  static constexpr int NDB = D / 32;   // 32-dim blocks of O^T
   static constexpr int NW = 8;         // waves per workgroup
   static constexpr int BR = 32 * NW;   // query rows per workgroup
   static constexpr int BC = 128;       // keys per LDS tile (two 64-key units)
@@ -55,14 +61,31 @@ struct Fp8Tile {
 constexpr int kP8Shift = 6;             // exponent offset of the stored probabilities
 constexpr float kP8Threshold = 2.f;     // reference raise threshold, exp2 units
 
-// K rows are read 16 keys at one logical chunk: bits 1..3 of the key spread
-// them over all eight 16-byte positions (the key's parity picks the other half
-// of the 64 banks).
-__device__ __forceinline__ int swz8(int key) { return (key >> 1) & 7; }
+// Swizzles of the 16-byte chunks of a key row in LDS (logical chunk ^ swz).
+// K rows are read 16 keys at one logical chunk. d = 128 (128-byte rows):
+// bits 1..3 of the key spread them over all eight positions, the key's parity
+// picks the other half of the 64 banks. d = 64 (64-byte rows, four keys per
+// bank sweep): bits 2..3 spread the four keys that share bank groups over the
+// four positions.
+template <int D>
+__device__ __forceinline__ int swz8(int key) {
+  if constexpr (D == 128)
+    return (key >> 1) & 7;
+  else
+    return (key >> 2) & 3;
+}
 // A transposing V read of a half-wave touches keys {0..3, 8..11} (+4) at two
-// adjacent chunks; bits 1 and 3 of the key move each key to its own pair of
-// positions, so the 8 keys x 2 chunks cover all 16 bank groups.
-__device__ __forceinline__ int swz8v(int key) { return 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1); }
+// adjacent chunks. d = 128: bits 1 and 3 of the key move each key to its own
+// pair of positions, so the 8 keys x 2 chunks cover all 16 bank groups. d = 64:
+// keys k and k + 8 share bank groups; bit 3 moves k + 8 to the other pair of
+// positions, so the 8 keys x 2 chunks x 2 halves cover all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz8v(int key) {
+  if constexpr (D == 128)
+    return 2 * ((key >> 1) & 1) + 4 * ((key >> 3) & 1);
+  else
+    return 2 * ((key >> 3) & 1);
+}
 
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -72,12 +95,12 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)(p));
 }
 
-template <bool CAUSAL>
+template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                        const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ LSE, int N, float lse_scale, float c2,
                                                        float v_descale, int n_qt, int BH) {
-  using T = Fp8Tile;
+  using T = Fp8Tile<HD>;
   constexpr int D = T::D;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::NBUF * T::KT];
 
@@ -94,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   const uint8_t* Vh = V + head;
   const int wq0 = q0 + 32 * w;
 
-  // copy instruction v of a tile moves keys 8v .. 8v + 7 (1 KB); lane l
+  // copy instruction v of a tile moves keys KPI*v .. + KPI - 1 (1 KB); lane l
   // fetches the logical chunk that its LDS position holds
   auto dma = [&](int j, int slot) __attribute__((always_inline)) {
     const uint32_t kb = lds_addr(lds) + slot * T::KT;
@@ -102,10 +125,11 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 #pragma unroll
     for (int i = 0; i < T::IPW; ++i) {
       const int v = w * T::IPW + i;
-      const int kr = 8 * v + (l >> 3);
+      const int kr = T::KPI * v + l / T::NCH;
+      const int pos = l % T::NCH;
       const size_t key = (size_t)min(j * T::BC + kr, N - 1);  // keys past N: any valid row, masked later
-      global_load_lds16(Kh + key * D + 16 * ((l & 7) ^ swz8(kr)), kb + v * 1024);
-      global_load_lds16(Vh + key * D + 16 * ((l & 7) ^ swz8v(kr)), vb + v * 1024);
+      global_load_lds16(Kh + key * D + 16 * (pos ^ swz8<D>(kr)), kb + v * 1024);
+      global_load_lds16(Vh + key * D + 16 * (pos ^ swz8v<D>(kr)), vb + v * 1024);
     }
   };
 
@@ -118,11 +142,11 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   if (n_kt > 1) dma(1, 1);
   // Q^T as the B operand: for MFMA c, lane (query lq, half hf) holds dims
   // 64c + 32hf .. + 31 (the same k-slots as the K rows of the A operand)
-  i32x8 qop[2];
+  i32x8 qop[T::NQ];
   {
     const int row = wq0 + lq;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < T::NQ; ++c) {
       if (row < N) {
         const u32x4 a = *(const u32x4*)(Qh + (size_t)row * D + 64 * c + 32 * hf);
         const u32x4 b = *(const u32x4*)(Qh + (size_t)row * D + 64 * c + 32 * hf + 16);
@@ -138,33 +162,35 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   // reads) for 32-dim block db: lane (group g, t) addresses key
   // 8*(e/4) + e%4 + 4*hf (e = t/2) of a 16-key group, chunk 2db + g%2, bytes
   // 8*(t%2) .. + 7 -> v_lane[db]; the key-group offsets are immediates.
-  int k_lane[4], v_lane[4];
+  int k_lane[2 * T::NQ], v_lane[T::NDB];
 #pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) k_lane[i4] = lq * D + 16 * ((4 * (i4 >> 1) + 2 * hf + (i4 & 1)) ^ swz8(lq));
+  for (int i4 = 0; i4 < 2 * T::NQ; ++i4)
+    k_lane[i4] = lq * D + 16 * ((4 * (i4 >> 1) + 2 * hf + (i4 & 1)) ^ swz8<D>(lq));
   {
     const int t = l & 15, g = l >> 4, e = t >> 1;
     const int key = 8 * (e >> 2) + (e & 3) + 4 * hf;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) v_lane[db] = T::VREG + key * D + 16 * ((2 * db + (g & 1)) ^ swz8v(key)) + 8 * (t & 1);
+    for (int db = 0; db < T::NDB; ++db)
+      v_lane[db] = T::VREG + key * D + 16 * ((2 * db + (g & 1)) ^ swz8v<D>(key)) + 8 * (t & 1);
   }
 
   // 64-key unit u lives in tile u / 2, keys 64 * (u % 2) .. of its slot
   auto unit_base = [](int u) { return ((u >> 1) & 3) * T::KT + (u & 1) * 64 * T::D; };
-  auto read_k = [&](i32x8(&kf)[2][2], int u) __attribute__((always_inline)) {
+  auto read_k = [&](i32x8(&kf)[2][T::NQ], int u) __attribute__((always_inline)) {
     const int base = unit_base(u);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < T::NQ; ++c) {
         const u32x4 a = *(const u32x4*)(lds + (k_lane[2 * c] + base) + st * 32 * D);
         const u32x4 b = *(const u32x4*)(lds + (k_lane[2 * c + 1] + base) + st * 32 * D);
         kf[st][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
       }
   };
-  auto read_v = [&](i32x8(&vf)[4], int u) __attribute__((always_inline)) {
+  auto read_v = [&](i32x8(&vf)[T::NDB], int u) __attribute__((always_inline)) {
     const int base = unit_base(u);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
+    for (int db = 0; db < T::NDB; ++db) {
       i32x2 part[4];
 #pragma unroll
       for (int rho = 0; rho < 4; ++rho) part[rho] = lds_read_tr8(lds + (v_lane[db] + base) + (16 * rho) * D);
@@ -173,20 +199,21 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
       vf[db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
-  auto qk = [&](f32x16(&s)[2], const i32x8(&kf)[2][2]) __attribute__((always_inline)) {
+  auto qk = [&](f32x16(&s)[2], const i32x8(&kf)[2][T::NQ]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       s[st] = mfma_fp8(kf[st][0], qop[0], (f32x16){});
-      s[st] = mfma_fp8(kf[st][1], qop[1], s[st]);
+#pragma unroll
+      for (int c = 1; c < T::NQ; ++c) s[st] = mfma_fp8(kf[st][c], qop[c], s[st]);
     }
   };
 
   f32x16 sA[2], sB[2];
-  f32x16 oacc[4];
-  i32x8 kf[2][2], pb = {};
+  f32x16 oacc[T::NDB];
+  i32x8 kf[2][T::NQ], pb = {};
   float m = -INFINITY, lsum = 0.f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = (f32x16){};
+  for (int db = 0; db < T::NDB; ++db) oacc[db] = (f32x16){};
 
   // One unit: P V for unit u from its scores `cur`, while the scores of unit
   // u + 1 are computed into `nxt` and the K rows of unit u + 2 are read. That
@@ -221,7 +248,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
       m = m_new;
       lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
@@ -243,10 +270,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
       pb[wd] = word;
     }
     lsum += ps;
-    i32x8 vf[4];
+    i32x8 vf[T::NDB];
     read_v(vf, u);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+    for (int db = 0; db < T::NDB; ++db) oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
   };
   // End of tile j: tile j + 2 resident for every wave and every wave done with
   // tile j, whose slot then receives tile j + 4.
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     const float f = v_descale / ltot;
     uint16_t* orow = O + (size_t)bh * N * D + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
         const bf16x2 a = to_bf16x2(oacc[db][4 * rb] * f, oacc[db][4 * rb + 1] * f);
@@ -292,10 +319,11 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   }
 }
 
-hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                          bool causal, float scale, float q_descale, float k_descale, float v_descale,
-                          hipStream_t s) {
-  using T = Fp8Tile;
+template <int D>
+static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                   int N, bool causal, float scale, float q_descale, float k_descale,
+                                   float v_descale, hipStream_t s) {
+  using T = Fp8Tile<D>;
   int n_qt = (N + T::BR - 1) / T::BR;
   int BH = B * H;
   float lse_scale = scale * q_descale * k_descale;  // logit = lse_scale * (Q8 . K8)
@@ -304,8 +332,16 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
   const uint8_t *qp = (const uint8_t*)q, *kp = (const uint8_t*)k, *vp = (const uint8_t*)v;
   uint16_t* op = (uint16_t*)o;
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &lse_scale, &c2, &v_descale, &n_qt, &BH};
-  const void* kern = causal ? (const void*)&fwd_fp8_kernel<true> : (const void*)&fwd_fp8_kernel<false>;
+  const void* kern = causal ? (const void*)&fwd_fp8_kernel<D, true> : (const void*)&fwd_fp8_kernel<D, false>;
   return hipLaunchKernel(kern, dim3((unsigned)(n_qt * BH)), dim3(64 * T::NW), args, 0, s);
+}
+
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                          int d, bool causal, float scale, float q_descale, float k_descale, float v_descale,
+                          hipStream_t s) {
+  if (d == 64)
+    return launch_fwd_fp8_t<64>(q, k, v, o, lse, B, H, N, causal, scale, q_descale, k_descale, v_descale, s);
+  return launch_fwd_fp8_t<128>(q, k, v, o, lse, B, H, N, causal, scale, q_descale, k_descale, v_descale, s);
 }
 
 }  // namespace fa

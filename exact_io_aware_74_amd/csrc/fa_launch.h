@@ -14,7 +14,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 
 // FP8 (e4m3) forward, d = 128: the logical inputs are descale * tensor.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                          bool causal, float scale, float q_descale, float k_descale, float v_descale,
+                          int d, bool causal, float scale, float q_descale, float k_descale, float v_descale,
                           hipStream_t s);
 
 // Decode: `chunk` keys per split, `nsplit` splits (every split non-empty).

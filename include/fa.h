@@ -92,7 +92,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  *   q, k, v     const FP8 e4m3 (OCP "fn" encoding, 1 byte) [B,H,N,d]
  *   o           bf16 [B,H,N,d]
  *   lse         float32 [B,H,N] or NULL: natural-log LSE of the scaled logits
- *   d           128 only (FA_ERR_UNSUPPORTED otherwise)
+ *   d           64 or 128 (FA_ERR_UNSUPPORTED otherwise)
  *   scale, q_descale, k_descale, v_descale: finite and >= 0
  * Arithmetic: Q K^T on FP8 MFMAs with fp32 accumulation; the probabilities
  * are rounded to e4m3 (nearest even, after an exact power-of-two scaling that

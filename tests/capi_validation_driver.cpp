@@ -21,8 +21,8 @@ hipError_t launch_fwd_bf16(const void*, const void*, const void*, void*, float*,
                            hipStream_t) { reached("fwd_bf16"); }
 hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, float*, int, int, int, int, bool, float,
                           hipStream_t) { reached("fwd_f32"); }
-hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, int, int, int, bool, float, float,
-                          float, float, hipStream_t) { reached("fwd_fp8"); }
+hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, int, int, int, int, bool, float,
+                          float, float, float, hipStream_t) { reached("fwd_fp8"); }
 hipError_t launch_decode(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
                          hipStream_t) { reached("decode"); }
 hipError_t launch_decode_paged(const void*, const void*, const void*, const int*, const int*, void*, float*, int, int,
@@ -89,7 +89,8 @@ int main() {
   auto f8 = [&](const void* q, void* o, float* lse, int N, int d, float s, float qd) {
     return fa_fwd_fp8(q, Bp, C, o, lse, 1, 1, N, d, 1, s, qd, 1.f, 1.f, nullptr);
   };
-  EXPECT(f8(A, Dp, L, 16, 64, 0.1f, 1.f), UNS);
+  EXPECT(f8(A, Dp, L, 16, 96, 0.1f, 1.f), UNS);
+  EXPECT(f8(A, Dp, L, 16, 32, 0.1f, 1.f), UNS);
   EXPECT(f8(A, Dp, L, 16, 128, nan, 1.f), INV);
   EXPECT(f8(A, Dp, L, 16, 128, 0.1f, -1.f), INV);
   EXPECT(f8(A, Dp, L, 16, 128, 0.1f, inf), INV);

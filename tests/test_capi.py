@@ -84,7 +84,8 @@ def test_fwd_fp8_validation(lib):
         return lib.fa_fwd_fp8(kw.get("q", A), kw.get("k", Bp), kw.get("v", C), kw.get("o", Dp), kw.get("lse", L),
                               kw.get("B", 1), kw.get("H", 1), kw.get("N", 16), kw.get("d", 128), kw.get("causal", 1),
                               kw.get("scale", 0.088), kw.get("qd", 0.01), kw.get("kd", 0.01), kw.get("vd", 0.01), None)
-    assert f8(d=64) == UNSUPPORTED                                   # FP8 path: d = 128 only
+    assert f8(d=96) == UNSUPPORTED                                   # FP8 path: d = 64 or 128
+    assert f8(d=32) == UNSUPPORTED
     assert f8(d=0) == INVALID
     for bad in (float("nan"), float("inf"), -1.0):
         assert f8(scale=bad) == INVALID

@@ -63,20 +63,22 @@ def fp8_case_run(q8, k8, v8, ds, causal, scale, rows=None, heads=None):
     return np.stack(got_o), np.stack(ref_o), np.stack(got_l), np.stack(ref_l), vmax
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 1000])
-def test_ragged_shapes(causal, N):
+def test_ragged_shapes(causal, N, d):
     B, H = (2, 3) if N <= 257 else (1, 2)
-    q8, k8, v8, ds = si.fp8_case(N + 7 * causal, B, H, N, 128)
-    go, ro, gl, rl, vmax = fp8_case_run(q8, k8, v8, ds, causal, fa.default_scale(128))
+    q8, k8, v8, ds = si.fp8_case(N + 7 * causal + d, B, H, N, d)
+    go, ro, gl, rl, vmax = fp8_case_run(q8, k8, v8, ds, causal, fa.default_scale(d))
     assert_fp8_close(go, ro, vmax)
     assert_lse_close(gl, rl, "bf16")
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("std", [0.25, 1.0, 3.0])
-def test_logit_ranges(std):
-    q8, k8, v8, ds = si.fp8_case(int(100 * std), 1, 4, 600, 128, std=std)
-    go, ro, gl, rl, vmax = fp8_case_run(q8, k8, v8, ds, True, fa.default_scale(128))
+def test_logit_ranges(std, d):
+    q8, k8, v8, ds = si.fp8_case(int(100 * std) + d, 1, 4, 600, d, std=std)
+    go, ro, gl, rl, vmax = fp8_case_run(q8, k8, v8, ds, True, fa.default_scale(d))
     print("fp8 std", std, assert_fp8_close(go, ro, vmax))
     assert_lse_close(gl, rl, "bf16")
 
