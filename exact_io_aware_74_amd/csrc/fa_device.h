@@ -79,6 +79,12 @@ __device__ __forceinline__ void agpr_fence(f32x16& acc) {
 __device__ __forceinline__ void global_load_lds16(const void* src, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds_addr) : "memory", "m0");
 }
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset: the address math stays on the scalar unit.
+__device__ __forceinline__ void global_load_lds16_s(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(N): at most N vector-memory operations of this wave remain
 // outstanding (loads complete in issue order). Issued through the builtin so
 // the compiler accounts for it in its own waits.

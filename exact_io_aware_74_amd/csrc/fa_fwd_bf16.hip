@@ -26,16 +26,19 @@
 //    XOR-swizzled per key, so K fragment reads and transposing V reads are
 //    free of bank conflicts and every read address is one of a few per-lane
 //    bases plus an immediate;
-//  * software pipeline over 32-key sub-tiles: in one basic block the wave
-//    turns sub-tile t's scores into probabilities and accumulates P V for t
-//    while the MFMAs for S(t+1) run; with two waves per SIMD the hardware
-//    also overlaps one wave's softmax with the other's MFMAs;
-//  * the running maximum is only raised when a sub-tile exceeds it by more
-//    than 2^8 in exp2 units (probabilities then stay <= 256: exact in fp32,
-//    representable in bf16). Rows that do not need it keep the old reference,
-//    which leaves O and the log-sum-exp unchanged mathematically, so the O
-//    rescale is rare and sits on a wave-uniform branch, as does the causal /
-//    ragged-tail mask;
+//  * software pipeline over 32-key sub-tiles: the wave turns sub-tile t's
+//    scores into probabilities while the MFMAs for S(t+1) run, then
+//    accumulates P V for t; with two waves per SIMD the hardware also
+//    overlaps one wave's softmax with the other's MFMAs;
+//  * probabilities are taken against a reference maximum that is raised only
+//    when needed: a sub-tile is accepted against the current reference if
+//    every lane's sum of its probabilities is at most 256 (so each of them
+//    is: exact in fp32 range, representable in bf16). Otherwise the wave
+//    takes the exact update (reference raised to the row maximum, O and the
+//    running sum rescaled) and recomputes the sub-tile's probabilities. Any
+//    reference leaves O and the log-sum-exp unchanged mathematically, so no
+//    per-sub-tile row maximum is computed, and the rare update sits on a
+//    wave-uniform branch, as does the causal / ragged-tail mask;
 //  * causal: key tiles past the workgroup's last query are never loaded and
 //    sub-tiles past a wave's last query are skipped by that wave;
 //  * heaviest causal query tiles are dispatched first, and consecutive
@@ -90,9 +93,12 @@ __device__ __forceinline__ void o_fence(f32x16 (&oacc)[QB][NDB]) {
   }
 }
 
-// Threshold (exp2 units) by which a sub-tile maximum must exceed the running
-// reference before the reference is raised and O rescaled.
-constexpr float kRescaleThreshold = 8.f;
+// Largest in-lane sum of a sub-tile's probabilities accepted against the
+// current reference maximum. Probabilities are non-negative, so the sum bounds
+// each of them: every probability that enters O and the row sum is at most
+// 256, exact in fp32 range and representable in bf16. A larger sum (or an
+// overflow to inf) sends the wave through the exact update instead.
+constexpr float kPsumLimit = 256.f;
 
 // A tile is stored row-major by 64-dim octets: octet o of key k is 128 bytes
 // at o*64*128 + k*128, so one copy instruction moves 8 keys x 128 contiguous
@@ -128,19 +134,41 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   // ---- DMA of one K/V tile into a ring slot: instruction v of the tile
   // (wave w issues v = w*IPW .. w*IPW + IPW - 1 for each tensor) copies octet
   // v / 8 of keys k0 + 8*(v % 8) .. + 7; lane l fetches the logical chunk that
-  // its LDS position holds ----
+  // its LDS position holds. A tile that lies inside [0, N) is addressed as a
+  // scalar tile base plus a per-lane byte offset that is the same for every
+  // tile (no vector address math per copy); the tile that crosses N clamps
+  // each key to N - 1 (any valid row: those keys are masked later) ----
+  uint32_t k_off[T::IPW], v_off[T::IPW];
+#pragma unroll
+  for (int i = 0; i < T::IPW; ++i) {
+    const int v = w * T::IPW + i, o = v >> 3, b = v & 7;
+    const int kr = 8 * b + (l >> 3);  // key within the tile
+    k_off[i] = 2u * (uint32_t)(kr * D + 64 * o + 8 * ((l & 7) ^ swz_k(kr)));
+    v_off[i] = 2u * (uint32_t)(kr * D + 64 * o + 8 * ((l & 7) ^ swz_v(kr)));
+  }
   auto dma = [&](int j, int slot) __attribute__((always_inline)) {
     const uint32_t kb = lds_addr(lds) + slot * T::KT;
     const uint32_t vb = kb + T::VREG;
+    if (j * T::BC + T::BC <= N) {
+      const uint16_t* kt = Kh + (size_t)j * (T::BC * D);
+      const uint16_t* vt = Vh + (size_t)j * (T::BC * D);
 #pragma unroll
-    for (int i = 0; i < T::IPW; ++i) {
-      const int v = w * T::IPW + i, o = v >> 3, b = v & 7;
-      const int kr = 8 * b + (l >> 3);  // key within the tile
-      const int key = min(j * T::BC + kr, N - 1);  // keys past N: any valid row, masked later
-      const uint16_t* src = Kh + (size_t)key * D + 64 * o;
-      global_load_lds16(src + 8 * ((l & 7) ^ swz_k(kr)), kb + o * (T::BC * 128) + b * 1024);
-      const uint16_t* vsrc = Vh + (size_t)key * D + 64 * o;
-      global_load_lds16(vsrc + 8 * ((l & 7) ^ swz_v(kr)), vb + o * (T::BC * 128) + b * 1024);
+      for (int i = 0; i < T::IPW; ++i) {
+        const int v = w * T::IPW + i, o = v >> 3, b = v & 7;
+        global_load_lds16_s(kt, k_off[i], kb + o * (T::BC * 128) + b * 1024);
+        global_load_lds16_s(vt, v_off[i], vb + o * (T::BC * 128) + b * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::IPW; ++i) {
+        const int v = w * T::IPW + i, o = v >> 3, b = v & 7;
+        const int kr = 8 * b + (l >> 3);
+        const int key = min(j * T::BC + kr, N - 1);
+        const uint16_t* src = Kh + (size_t)key * D + 64 * o;
+        global_load_lds16(src + 8 * ((l & 7) ^ swz_k(kr)), kb + o * (T::BC * 128) + b * 1024);
+        const uint16_t* vsrc = Vh + (size_t)key * D + 64 * o;
+        global_load_lds16(vsrc + 8 * ((l & 7) ^ swz_v(kr)), vb + o * (T::BC * 128) + b * 1024);
+      }
     }
   };
 
@@ -189,7 +217,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   f32x16 oacc[QB][T::NDB];  // O^T (AGPRs): lane l owns query l % 32 of each block
   float m[QB];              // reference maximum of the raw scores q.k
   float lsum[QB];           // this half-wave's share of the running sum
-  float mt[QB];             // maximum of the pending sub-tile
+  float mt[QB];             // maximum of a sub-tile (exact update only)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -237,36 +265,46 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
       }
     }
   };
-  // Raise the reference maximum where a row's new sub-tile exceeds it by more
-  // than the threshold (wave-uniform branch; every lane then takes the exact
-  // online-softmax update, with alpha = 1 where its maximum did not move).
-  auto maybe_rescale = [&]() __attribute__((always_inline)) {
-    bool need = false;
+  // The exact online-softmax update for sub-tile s: the reference maximum
+  // of every row becomes max(m, rowmax s) and O and the running sum are
+  // rescaled by alpha = exp2((m_old - m_new) c2) (alpha = 1 where the
+  // maximum did not move). Returns alpha per query block.
+  auto raise_ref = [&](const f32x16(&s)[QB], float(&alpha)[QB]) __attribute__((always_inline)) {
+    tile_max(s);
+    o_fence(oacc);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) need = need || (mt[qb] - m[qb]) * c2 > kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      o_fence(oacc);
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = fmaxf(m[qb], mt[qb]);
+      alpha[qb] = fast_exp2((m[qb] - m_new) * c2);
+      m[qb] = m_new;
+      lsum[qb] *= alpha[qb];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float m_new = fmaxf(m[qb], mt[qb]);
-        const float alpha = fast_exp2((m[qb] - m_new) * c2);
-        m[qb] = m_new;
-        lsum[qb] *= alpha;
+      for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-      }
+        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
     }
+  };
+  // True (wave-uniform) when some lane's probability sum is above the limit
+  // or not finite.
+  auto over_limit = [&](const float(&x)[QB]) __attribute__((always_inline)) {
+    bool bad = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) bad = bad || !(x[qb] <= kPsumLimit);
+    return __builtin_amdgcn_ballot_w64(bad) != 0;
   };
   // Probabilities of a sub-tile against the reference maximum: bf16 B operand
   // of P V and this half-wave's fp32 row sums. One call handles elements r,
   // r + 1 of query block qb (mc = reference maximum in exp2 units).
-  auto prob_pair = [&](const f32x16(&s)[QB], bf16x8(&pb)[QB][2], float(&ps)[QB], const float(&mc)[QB], int qb,
-                       int r) __attribute__((always_inline)) {
+  // The sum goes to ps0 for the first 16-key chunk (elements 0-7) and to ps1
+  // for the second: two independent add chains.
+  auto prob_pair = [&](const f32x16(&s)[QB], bf16x8(&pb)[QB][2], float(&ps0)[QB], float(&ps1)[QB],
+                       const float(&mc)[QB], int qb, int r) __attribute__((always_inline)) {
     const float p0 = fast_exp2(fmaf(s[qb][r], c2, -mc[qb]));
     const float p1 = fast_exp2(fmaf(s[qb][r + 1], c2, -mc[qb]));
-    ps[qb] += p0 + p1;
+    if (r < 8)
+      ps0[qb] += p0 + p1;
+    else
+      ps1[qb] += p0 + p1;
     const bf16x2 two = to_bf16x2(p0, p1);
     pb[qb][r >> 3][r & 7] = two[0];
     pb[qb][r >> 3][(r & 7) + 1] = two[1];
@@ -290,26 +328,31 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   // t % 2), score sub-tile t + 1 (needs t + 1 < n_st; its first two K
   // fragments are already in kf, the others are read two k-chunks ahead) and
   // fetch the first K fragments of sub-tile t + 2 (half t % 2 of the slot at
-  // kp_slot). The source order is the intended issue order, so that the
-  // matrix core has independent work at every point: the score MFMAs of t + 1
-  // with most probabilities of t and the first V^T reads between them, then
-  // the P V MFMAs of t with the last probabilities and V^T reads, the row
-  // maximum of t + 1 and the next K fragments. With two waves per SIMD the
-  // hardware interleaves the waves; pinning the order further with
-  // scheduling fences measured no better.
+  // kp_slot). The source order is the intended issue order: the score MFMAs
+  // of t + 1 with the probabilities of t and the first V^T reads between
+  // them, then the P V MFMAs of t with the other V^T reads and the next K
+  // fragments. With two waves per SIMD the hardware interleaves the waves.
+  //
+  // Probabilities are taken against the current reference maximum. Before
+  // P V reads them the wave checks their in-lane sums: if one is above
+  // kPsumLimit (or not finite), the wave takes the exact update for sub-tile
+  // t and recomputes its probabilities. No row maximum is computed otherwise.
+  // (Checking each 16-key half just before its P V products, so that part of
+  // the probabilities could still be computed under the P V MFMAs, keeps the
+  // sub-tile's scores live across more code and spills at d = 128.)
   auto step_body = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
     const int h = t & 1;
     const int kp_slot_cur = h ? kp_slot : v_slot;  // slot of sub-tile t + 1 (rest of its K fragments)
     bf16x8 vf[2][T::NDB], pb[QB][2];
-    float ps[QB], mc[QB], mx[QB];
+    float ps0[QB], ps1[QB], mc[QB], alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ps[qb] = 0.f;
+      ps0[qb] = 0.f;
+      ps1[qb] = 0.f;
       mc[qb] = m[qb] * c2;
-      mx[qb] = -INFINITY;
     }
-    constexpr int EARLY = 3 * NPAIR / 4;  // pairs computed under the score MFMAs
+    constexpr int EARLY = NPAIR;  // every pair is computed under the score MFMAs
     // The score MFMAs run at raised wave priority: when both waves of a SIMD
     // can issue, the one feeding the matrix core goes first (measured 1-2%).
     __builtin_amdgcn_s_setprio(1);
@@ -320,60 +363,70 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
       if (c + 2 < T::NC) kf[c + 2] = k_frag(kp_slot_cur, (t + 1) & 1, c + 2);
 #pragma unroll
       for (int i = EARLY * c / T::NC; i < EARLY * (c + 1) / T::NC; ++i)
-        prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
+        prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
       if (c < T::NDB) vf[0][c] = load_v(v_slot, h, 0, c);  // the 16-key chunk kc = 1 follows below
     }
     __builtin_amdgcn_s_setprio(0);
-    constexpr int PER = 16 / (2 * T::NDB);  // max elements per query block per head-dim block
+    {
+      float chk[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) chk[qb] = ps0[qb] + ps1[qb];
+      if (over_limit(chk)) {
+        raise_ref(cur, alpha);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          ps0[qb] = 0.f;
+          ps1[qb] = 0.f;
+          mc[qb] = m[qb] * c2;
+        }
+#pragma unroll
+        for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 2 * T::NDB; ++i) {
       const int kc = i / T::NDB, db = i % T::NDB;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], vf[kc][db], pb[qb][kc]);
-      if (i < T::NDB) {
-#pragma unroll
-        for (int p = EARLY + (NPAIR - EARLY) * i / T::NDB; p < EARLY + (NPAIR - EARLY) * (i + 1) / T::NDB; ++p)
-          prob_pair(cur, pb, ps, mc, pair_qb(p), pair_r(p));
-        vf[1][i] = load_v(v_slot, h, 1, i);
-      }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int e = 0; e < PER; ++e) mx[qb] = fmaxf(mx[qb], nxt[qb][i * PER + e]);
+      if (i < T::NDB) vf[1][i] = load_v(v_slot, h, 1, i);
       if (i >= 2 * T::NDB - 2) kf[i - (2 * T::NDB - 2)] = k_frag(kp_slot, h, i - (2 * T::NDB - 2));
     }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      lsum[qb] += ps[qb];
-      mt[qb] = halves_max(mx[qb]);
-    }
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps0[qb] + ps1[qb];
   };
   // the same when sub-tile t + 1 is known to be fully visible
   auto clean_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
-                        __attribute__((always_inline)) {
-    step_body(cur, nxt, t, v_slot, kp_slot);
-    maybe_rescale();
-  };
+                        __attribute__((always_inline)) { step_body(cur, nxt, t, v_slot, kp_slot); };
   auto full_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
     step_body(cur, nxt, t, v_slot, kp_slot);
-    if (needs_mask(t + 1)) {
-      mask(nxt, t + 1);
-      tile_max(nxt);
-    }
-    maybe_rescale();
+    if (needs_mask(t + 1)) mask(nxt, t + 1);
   };
   // the wave's last sub-tile: probabilities and P V only
   auto last_step = [&](f32x16(&cur)[QB], int t, int v_slot) __attribute__((always_inline)) {
     bf16x8 pb[QB][2];
-    float ps[QB], mc[QB];
+    float ps0[QB], ps1[QB], mc[QB], alpha[QB], chk[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ps[qb] = 0.f;
+      ps0[qb] = 0.f;
+      ps1[qb] = 0.f;
       mc[qb] = m[qb] * c2;
     }
 #pragma unroll
-    for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps, mc, pair_qb(i), pair_r(i));
+    for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) chk[qb] = ps0[qb] + ps1[qb];
+    if (over_limit(chk)) {
+      raise_ref(cur, alpha);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        ps0[qb] = 0.f;
+        ps1[qb] = 0.f;
+        mc[qb] = m[qb] * c2;
+      }
+#pragma unroll
+      for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
+    }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -383,7 +436,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
         for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], a, pb[qb][kc]);
       }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps[qb];
+    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps0[qb] + ps1[qb];
   };
   auto tail_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
                        __attribute__((always_inline)) {
@@ -396,13 +449,13 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   // the next step on) and every wave done with tile j, whose ring slot then
   // receives tile j + 4. A wave's copies complete in issue order, so with
   // tile j + 3 also in flight it waits until only that tile's copies remain.
-  auto end_tile = [&](int j) __attribute__((always_inline)) {
+  auto end_tile = [&](int j, int slot) __attribute__((always_inline)) {
     if (j + 3 < n_kt)
       wait_vmcnt<2 * T::IPW>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (j + 4 < n_kt) dma(j + 4, j & 3);
+    if (j + 4 < n_kt) dma(j + 4, slot);
   };
 
   wait_vmcnt<0>();  // Q, tiles 0 and 1
@@ -410,33 +463,47 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   if (n_kt > 2) dma(2, 2);
   if (n_kt > 3) dma(3, 3);
   if (n_st > 0) {
+    // sub-tile 0 sets the first reference (from m = -inf: alpha = 0)
+    float alpha0[QB];
     qk(sA, 0, 0);
     if (needs_mask(0)) mask(sA, 0);
-    tile_max(sA);
-    maybe_rescale();
+    raise_ref(sA, alpha0);
   }
   kf[0] = k_frag(0, 1, 0);  // sub-tile 1 (tile 0, second half)
   kf[1] = k_frag(0, 1, 1);
   // Leading sub-tiles that need no mask: the steady-state loop runs the tiles
   // whose both steps start such a sub-tile, with no branch but the rare
-  // rescale; the remaining tiles (diagonal, ragged end, or waves that are
+  // exact update; the remaining tiles (diagonal, ragged end, or waves that are
   // done and only help with the copies) go through the general step. Tile j
   // sits in ring slot j % 4. Steps past a wave's last sub-tile fetch unused
   // (in-range) K fragments.
   const int n_clean = min(CAUSAL ? (wq0 + 1) / 32 : N / 32, N / 32);
   const int j_clean = max(0, (n_clean - 1) / 2);
+  // The steady-state loop is unrolled over the ring depth, so every ring
+  // slot offset is a compile-time constant that folds into the LDS
+  // instructions' immediate offsets (j is a multiple of 4 at its top).
+  static_assert(T::NBUF == 4, "the unrolled loop walks a 4-slot ring");
   int j = 0;
+  for (; j + 4 <= j_clean; j += 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s0 = r * T::KT, s1 = ((r + 1) & 3) * T::KT;
+      clean_step(sA, sB, 2 * (j + r), s0, s1);
+      clean_step(sB, sA, 2 * (j + r) + 1, s0, s1);
+      end_tile(j + r, r);
+    }
+  }
   for (; j < j_clean; ++j) {
     const int s0 = (j & 3) * T::KT, s1 = ((j + 1) & 3) * T::KT;
     clean_step(sA, sB, 2 * j, s0, s1);
     clean_step(sB, sA, 2 * j + 1, s0, s1);
-    end_tile(j);
+    end_tile(j, j & 3);
   }
   for (; j < n_kt; ++j) {
     const int s0 = (j & 3) * T::KT, s1 = ((j + 1) & 3) * T::KT;
     tail_step(sA, sB, 2 * j, s0, s1);
     tail_step(sB, sA, 2 * j + 1, s0, s1);
-    end_tile(j);
+    end_tile(j, j & 3);
   }
 
   // ---- epilogue: O = acc / l, one rounding to bf16; LSE in natural log ----
