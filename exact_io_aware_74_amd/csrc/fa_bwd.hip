@@ -65,6 +65,18 @@ __device__ __forceinline__ void copy_part(const uint16_t* base, int r0, int rows
   const int row = min(r0 + rr, rows - 1);
   global_load_lds16(base + (size_t)row * D + 64 * o + 8 * ((l & 7) ^ bswz(rr)), dst + o * (BT * 128) + b * 1024);
 }
+// The same copy for a tile that lies inside the matrix: a scalar tile base
+// plus lane l's byte offset for instruction v (copy_off), which is the same
+// for every tile, so no vector address math is spent per copy.
+template <int D>
+__device__ __forceinline__ uint32_t copy_off(int v, int l) {
+  const int o = v >> 3, b = v & 7;
+  const int rr = 8 * b + (l >> 3);
+  return 2u * (uint32_t)(rr * D + 64 * o + 8 * ((l & 7) ^ bswz(rr)));
+}
+__device__ __forceinline__ void copy_part_s(const uint16_t* tile_base, uint32_t off, uint32_t dst, int v) {
+  global_load_lds16_s(tile_base, off, dst + (v >> 3) * (BT * 128) + (v & 7) * 1024);
+}
 
 // Per-lane byte offsets into a tile. Row fragment (MFMA A or B operand taken
 // along a row): row 32*h + lq, logical chunk 2c + hf -> row_lane[c % 4] +
@@ -183,16 +195,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const int qt0 = CAUSAL ? k0 / BT : 0;  // earlier query tiles see none of these keys
   const int n_t = n_qt > qt0 ? n_qt - qt0 : 0;  // query tiles this workgroup visits
   // ring of three slots: tile t (counted from qt0) sits in slot t % 3
-  auto copy = [&](int t) __attribute__((always_inline)) {
-    const int qt = qt0 + t;
-    const uint32_t base = lds_addr(lds) + (t % 3) * SLOT;
+  uint32_t coff[IPW];
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int v = w * IPW + i;  // 0 .. NCOPY - 1: Q, then dO
-      if (v < T::NCOPY)
-        copy_part<D>(Qh, qt * BT, N, base, v, l);
-      else
-        copy_part<D>(dOh, qt * BT, N, base + T::BYTES, v - T::NCOPY, l);
+  for (int i = 0; i < IPW; ++i) coff[i] = copy_off<D>((w * IPW + i) % T::NCOPY, l);
+  auto copy = [&](int t, int slot) __attribute__((always_inline)) {
+    const int qt = qt0 + t;
+    const uint32_t base = lds_addr(lds) + slot * SLOT;
+    if (qt * BT + BT <= N) {
+      const uint16_t* qtile = Qh + (size_t)qt * (BT * D);
+      const uint16_t* dotile = dOh + (size_t)qt * (BT * D);
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int v = w * IPW + i;  // 0 .. NCOPY - 1: Q, then dO
+        if (v < T::NCOPY)
+          copy_part_s(qtile, coff[i], base, v);
+        else
+          copy_part_s(dotile, coff[i], base + T::BYTES, v - T::NCOPY);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int v = w * IPW + i;
+        if (v < T::NCOPY)
+          copy_part<D>(Qh, qt * BT, N, base, v, l);
+        else
+          copy_part<D>(dOh, qt * BT, N, base + T::BYTES, v - T::NCOPY, l);
+      }
     }
     if (w == 0 && l < 32) {  // LSE2 then D of the tile's 64 rows (the workspace is padded)
       const float* src = (l < 16 ? L2h : Dh) + qt * BT + 4 * (l & 15);
@@ -200,13 +228,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
     }
   };
 
-  // 32-query block b: rows (qt0 + b/2) * 64 + 32 * (b % 2) .. + 31, in tile b / 2
+  // 32-query block b: rows (qt0 + b/2) * 64 + 32 * (b % 2) .. + 31, in tile
+  // b / 2, whose ring slot the callers pass as a byte offset (tQ)
   auto blk_q0 = [&](int b) { return (qt0 + (b >> 1)) * BT + 32 * (b & 1); };
-  auto blk_tile = [](int b) { return ((b >> 1) % 3) * SLOT; };
   // Row fragments (A operands of S and dP) of block b. Blocks past the end
   // read an in-range ring slot; the values are never used.
-  auto read_rows = [&](bf16x8(&rq)[T::NC], bf16x8(&rd)[T::NC], int b) __attribute__((always_inline)) {
-    const int tQ = blk_tile(b), h = b & 1;
+  auto read_rows = [&](bf16x8(&rq)[T::NC], bf16x8(&rd)[T::NC], int tQ, int b) __attribute__((always_inline)) {
+    const int h = b & 1;
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
       rq[c] = row_frag(lds, tQ, tl, h, c);
@@ -233,8 +261,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   // of block b + 2 are read into the registers those MFMAs consumed; dV and
   // dK accumulate.
   // Lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf.
+  // tQ: ring slot offset of block b's tile; tQ2: that of block b + 2's.
   auto block = [&](f32x16& sc, f32x16& dp, f32x16& sc_n, f32x16& dp_n, const bf16x8(&rq_n)[T::NC],
-                   const bf16x8(&rd_n)[T::NC], bf16x8(&rq_f)[T::NC], bf16x8(&rd_f)[T::NC], int b)
+                   const bf16x8(&rd_n)[T::NC], bf16x8(&rq_f)[T::NC], bf16x8(&rd_f)[T::NC], int b, int tQ, int tQ2)
                    __attribute__((always_inline)) {
     // A block before the diagonal (causal) or past the last row has every
     // score masked, so its P and dS are exactly 0 and it adds nothing.
@@ -249,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
         }
       }
     }
-    const int tQ = blk_tile(b), tdO = tQ + T::BYTES, h = b & 1;
+    const int tdO = tQ + T::BYTES, h = b & 1;
     const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
     auto read_stats = [&](f32x4& L, f32x4& Dv, int rb) __attribute__((always_inline)) {
       L = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
@@ -294,7 +323,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
       sc_n = mfma32x32x16(rq_n[c], kT[c], sc_n);
       dp_n = mfma32x32x16(rd_n[c], vT[c], dp_n);
     }
-    read_rows(rq_f, rd_f, b + 2);
+    read_rows(rq_f, rd_f, tQ2, b + 2);
     // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
     // the lane's queries), B = dO / Q through the transposing read
 #pragma unroll
@@ -317,22 +346,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   // Tile t + 1 is resident while tile t is processed (block 2t + 1 reads the
   // rows of the first block of tile t + 1); tile t + 2 is copied during tile
   // t into the slot of tile t - 1 and published by the barrier that ends t.
-  if (n_t > 0) copy(0);
-  if (n_t > 1) copy(1);
+  if (n_t > 0) copy(0, 0);
+  if (n_t > 1) copy(1, 1);
   wait_vmcnt<0>();
   __syncthreads();
   f32x16 scA, dpA, scB, dpB;
   bf16x8 rqA[T::NC], rdA[T::NC], rqB[T::NC], rdB[T::NC];
-  read_rows(rqA, rdA, 0);
+  read_rows(rqA, rdA, 0, 0);
   score(scA, dpA, rqA, rdA);
-  read_rows(rqB, rdB, 1);
-  for (int t = 0; t < n_t; ++t) {
-    if (t + 2 < n_t) copy(t + 2);
-    block(scA, dpA, scB, dpB, rqB, rdB, rqA, rdA, 2 * t);
-    block(scB, dpB, scA, dpA, rqA, rdA, rqB, rdB, 2 * t + 1);
+  read_rows(rqB, rdB, 0, 1);
+  // tile t in ring slot s (= t % 3); the next tile in s1, the copy target s2
+  auto tile = [&](int t, int s, int s1, int s2) __attribute__((always_inline)) {
+    if (t + 2 < n_t) copy(t + 2, s2);
+    block(scA, dpA, scB, dpB, rqB, rdB, rqA, rdA, 2 * t, s * SLOT, s1 * SLOT);
+    block(scB, dpB, scA, dpA, rqA, rdA, rqB, rdB, 2 * t + 1, s * SLOT, s1 * SLOT);
     wait_vmcnt<0>();
     __syncthreads();
+  };
+  // Unrolled over the ring depth (t is a multiple of 3 at the top), so every
+  // slot offset is a compile-time constant folded into the LDS instructions.
+  int t = 0;
+  for (; t + 3 <= n_t; t += 3) {
+    tile(t, 0, 1, 2);
+    tile(t + 1, 1, 2, 0);
+    tile(t + 2, 2, 0, 1);
   }
+  for (; t < n_t; ++t) tile(t, t % 3, (t + 1) % 3, (t + 2) % 3);
 
   // lane l holds head dim 32*db + lq of keys kw0 + (r%4) + 8(r/4) + 4hf
 #pragma unroll
@@ -393,23 +432,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
   const int n_kt = (kv_end + BT - 1) / BT;
   const int wv_end = CAUSAL ? min(N, wq0 + 32) : N;
   const int n_st = wq0 < N ? (wv_end + 31) / 32 : 0;  // 32-key sub-tiles this wave needs
+  uint32_t coff[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) coff[i] = copy_off<D>((w * IPW + i) % T::NCOPY, l);
   auto copy = [&](int j, int slot) __attribute__((always_inline)) {
     const uint32_t base = lds_addr(lds) + slot * SLOT;
+    if (j * BT + BT <= N) {
+      const uint16_t* ktile = Kh + (size_t)j * (BT * D);
+      const uint16_t* vtile = Vh + (size_t)j * (BT * D);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) {
-      const int v = w * IPW + i;
-      if (v < T::NCOPY)
-        copy_part<D>(Kh, j * BT, N, base, v, l);
-      else
-        copy_part<D>(Vh, j * BT, N, base + T::BYTES, v - T::NCOPY, l);
+      for (int i = 0; i < IPW; ++i) {
+        const int v = w * IPW + i;
+        if (v < T::NCOPY)
+          copy_part_s(ktile, coff[i], base, v);
+        else
+          copy_part_s(vtile, coff[i], base + T::BYTES, v - T::NCOPY);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < IPW; ++i) {
+        const int v = w * IPW + i;
+        if (v < T::NCOPY)
+          copy_part<D>(Kh, j * BT, N, base, v, l);
+        else
+          copy_part<D>(Vh, j * BT, N, base + T::BYTES, v - T::NCOPY, l);
+      }
     }
   };
 
   if (n_kt > 0) copy(0, 0);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int j = 0; j < n_kt; ++j) {
-    const int slot = j & 1;
+  // key tile j in ring slot `slot` (= j % 2)
+  auto tile = [&](int j, int slot) __attribute__((always_inline)) {
     if (j + 1 < n_kt) copy(j + 1, slot ^ 1);
     const int tK = slot * SLOT, tV = tK + T::BYTES;
 #pragma unroll
@@ -452,7 +507,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
     }
     wait_vmcnt<0>();
     __syncthreads();
+  };
+  // unrolled over the two ring slots (j is even at the top), so the slot
+  // offsets are compile-time constants
+  int j = 0;
+  for (; j + 2 <= n_kt; j += 2) {
+    tile(j, 0);
+    tile(j + 1, 1);
   }
+  if (j < n_kt) tile(j, 0);
 
   // lane l holds query qrow, head dims 32*db + (r%4) + 8(r/4) + 4hf
   if (qrow < N) {
