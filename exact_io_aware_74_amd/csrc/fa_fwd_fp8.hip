@@ -174,10 +174,10 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
       v_lane[db] = T::VREG + key * D + 16 * ((2 * db + (g & 1)) ^ swz8v<D>(key)) + 8 * (t & 1);
   }
 
-  // 64-key unit u lives in tile u / 2, keys 64 * (u % 2) .. of its slot
+  // 64-key unit u lives in tile u / 2, keys 64 * (u % 2) .. of its slot;
+  // read_k and read_v take that byte offset (base)
   auto unit_base = [](int u) { return ((u >> 1) & 3) * T::KT + (u & 1) * 64 * T::D; };
-  auto read_k = [&](i32x8(&kf)[2][T::NQ], int u) __attribute__((always_inline)) {
-    const int base = unit_base(u);
+  auto read_k = [&](i32x8(&kf)[2][T::NQ], int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -187,8 +187,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
         kf[st][c] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
       }
   };
-  auto read_v = [&](i32x8(&vf)[T::NDB], int u) __attribute__((always_inline)) {
-    const int base = unit_base(u);
+  auto read_v = [&](i32x8(&vf)[T::NDB], int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db) {
       i32x2 part[4];
@@ -221,11 +220,12 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   // possibly being refilled) into fragments nobody uses, and it keeps the
   // fragments in one set of registers (a conditional read costs a 32-register
   // copy per unit).
-  auto step = [&](f32x16(&cur)[2], f32x16(&nxt)[2], int u) __attribute__((always_inline)) {
+  // (the ring offsets of units u and u + 2 come in as vb_u and kb_u2)
+  auto step = [&](f32x16(&cur)[2], f32x16(&nxt)[2], int u, int vb_u, int kb_u2) __attribute__((always_inline)) {
     if (u >= n_u) return;
     if (u + 1 < n_u) {
       qk(nxt, kf);
-      read_k(kf, u + 2);
+      read_k(kf, kb_u2);
     }
     if ((64 * u + 64 > N) || (CAUSAL && 64 * u + 63 > wq0)) {
 #pragma unroll
@@ -271,19 +271,19 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     }
     lsum += ps;
     i32x8 vf[T::NDB];
-    read_v(vf, u);
+    read_v(vf, vb_u);
 #pragma unroll
     for (int db = 0; db < T::NDB; ++db) oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
   };
   // End of tile j: tile j + 2 resident for every wave and every wave done with
   // tile j, whose slot then receives tile j + 4.
-  auto end_tile = [&](int j) __attribute__((always_inline)) {
+  auto end_tile = [&](int j, int slot) __attribute__((always_inline)) {
     if (j + 3 < n_kt)
       wait_vmcnt<2 * T::IPW>();
     else
       wait_vmcnt<0>();
     __syncthreads();
-    if (j + 4 < n_kt) dma(j + 4, j & 3);
+    if (j + 4 < n_kt) dma(j + 4, slot);
   };
 
   wait_vmcnt<0>();  // Q, tiles 0 and 1
@@ -291,14 +291,26 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   if (n_kt > 2) dma(2, 2);
   if (n_kt > 3) dma(3, 3);
   if (n_u > 0) {
-    read_k(kf, 0);
+    read_k(kf, unit_base(0));
     qk(sA, kf);
-    if (n_u > 1) read_k(kf, 1);
+    if (n_u > 1) read_k(kf, unit_base(1));
   }
-  for (int j = 0; j < n_kt; ++j) {
-    step(sA, sB, 2 * j);
-    step(sB, sA, 2 * j + 1);
-    end_tile(j);
+  // Unrolled over the 4-slot ring (j is a multiple of 4 at its top), so every
+  // ring offset is a compile-time constant folded into the LDS instructions.
+  static_assert(T::NBUF == 4, "the unrolled loop walks a 4-slot ring");
+  int j = 0;
+  for (; j + 4 <= n_kt; j += 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      step(sA, sB, 2 * (j + r), unit_base(2 * r), unit_base(2 * r + 2));
+      step(sB, sA, 2 * (j + r) + 1, unit_base(2 * r + 1), unit_base(2 * r + 3));
+      end_tile(j + r, r);
+    }
+  }
+  for (; j < n_kt; ++j) {
+    step(sA, sB, 2 * j, unit_base(2 * j), unit_base(2 * j + 2));
+    step(sB, sA, 2 * j + 1, unit_base(2 * j + 1), unit_base(2 * j + 3));
+    end_tile(j, j & 3);
   }
 
   // ---- epilogue: O = v_descale * acc / l, one rounding to bf16; LSE in natural log ----
