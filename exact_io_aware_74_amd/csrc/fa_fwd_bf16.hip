@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     bool bad = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) bad = bad || !(x[qb] <= kPsumLimit);
-    return __builtin_amdgcn_ballot_w64(bad) != 0;
+    return __builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0);
   };
   // Probabilities of a sub-tile against the reference maximum: bf16 B operand
   // of P V and this half-wave's fp32 row sums. One call handles elements r,
@@ -348,8 +348,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     float ps0[QB], ps1[QB], mc[QB], alpha[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ps0[qb] = 0.f;
-      ps1[qb] = 0.f;
+      ps0[qb] = -0.f;  // x + (-0) = x exactly, so the first add folds away
+      ps1[qb] = -0.f;
       mc[qb] = m[qb] * c2;
     }
     constexpr int EARLY = NPAIR;  // every pair is computed under the score MFMAs
@@ -375,8 +375,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
         raise_ref(cur, alpha);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          ps0[qb] = 0.f;
-          ps1[qb] = 0.f;
+          ps0[qb] = -0.f;
+          ps1[qb] = -0.f;
           mc[qb] = m[qb] * c2;
         }
 #pragma unroll
@@ -408,8 +408,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     float ps0[QB], ps1[QB], mc[QB], alpha[QB], chk[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      ps0[qb] = 0.f;
-      ps1[qb] = 0.f;
+      ps0[qb] = -0.f;
+      ps1[qb] = -0.f;
       mc[qb] = m[qb] * c2;
     }
 #pragma unroll
@@ -420,8 +420,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
       raise_ref(cur, alpha);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        ps0[qb] = 0.f;
-        ps1[qb] = 0.f;
+        ps0[qb] = -0.f;
+        ps1[qb] = -0.f;
         mc[qb] = m[qb] * c2;
       }
 #pragma unroll
