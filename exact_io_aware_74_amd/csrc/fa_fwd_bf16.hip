@@ -534,7 +534,8 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
 #endif
 // query blocks of 32 rows per wave: 1 = eight waves (two per SIMD, the
 // hardware interleaves them), 2 = four waves with every LDS fragment feeding
-// two MFMAs
+// two MFMAs (with every probability computed under the score MFMAs, that
+// variant keeps both blocks' probabilities live and spills at d = 128)
 constexpr int kFwdQB = FA_FWD_QB;
 
 template <int D, bool CAUSAL>
