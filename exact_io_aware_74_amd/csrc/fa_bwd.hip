@@ -12,8 +12,10 @@
 //   dQ = scale dS K,   dK = scale dS^T Q.
 //
 // Three kernels:
-//  * bwd_prep: D (fp32) and LSE * log2(e) per query row, into the caller's
-//    workspace (rows padded to a multiple of 64 with zeros);
+//  * bwd_prep: -D (fp32) and LSE * log2(e) per query row, into the caller's
+//    workspace (rows padded to a multiple of 64 with zeros). The other two
+//    kernels start each dP accumulation from -D, so the MFMA result is
+//    already dP - D and dS = P * (dP - D) costs one multiply per element;
 //  * bwd_dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys). A
 //    wave keeps its keys' K and V rows in VGPRs as MFMA B operands and streams
 //    64-row Q / dO tiles through LDS. Per 32 queries it recomputes
@@ -116,7 +118,7 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// ---- D = rowsum(dO * O) and LSE in exp2 units, per query row ----
+// ---- -D = -rowsum(dO * O) and LSE in exp2 units, per query row ----
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE, float* __restrict__ lse2,
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
   if (part == 0 && bh < BH) {
     lse2[prow] = valid ? LSE[(size_t)bh * N + i] * kLog2e : 0.f;
-    Dsum[prow] = valid ? acc : 0.f;
+    Dsum[prow] = valid ? -acc : 0.f;  // stored negated: the dP accumulations start from it
   }
 }
 
@@ -241,12 +243,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
       rd[c] = row_frag(lds, tQ + T::BYTES, tl, h, c);
     }
   };
-  auto score = [&](f32x16& sc, f32x16& dp, const bf16x8(&rq)[T::NC], const bf16x8(&rd)[T::NC])
+  // -D of the 32 queries of half hh of the tile at byte offset `tile`, in
+  // accumulator order (element r: query (r%4) + 8(r/4) + 4hf of the half)
+  auto neg_d = [&](int tile, int hh) __attribute__((always_inline)) {
+    const float* st = (const float*)(lds + tile + 2 * T::BYTES) + BT + 32 * hh + 4 * hf;
+    f32x16 r;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 x = *(const f32x4*)(st + 8 * rb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[4 * rb + i] = x[i];
+    }
+    return r;
+  };
+  // S and dP - D of one block (dP accumulated from -D)
+  auto score = [&](f32x16& sc, f32x16& dp, const bf16x8(&rq)[T::NC], const bf16x8(&rd)[T::NC], const f32x16& nd)
                    __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
       sc = mfma32x32x16(rq[c], kT[c], c == 0 ? (f32x16){} : sc);
-      dp = mfma32x32x16(rd[c], vT[c], c == 0 ? (f32x16){} : dp);
+      dp = mfma32x32x16(rd[c], vT[c], c == 0 ? nd : dp);
     }
   };
   // One block b. With one wave per SIMD the wave issues in order, so the
@@ -274,30 +290,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
         const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
         if (!(q < N && (!CAUSAL || key <= q))) {
           sc[r] = -INFINITY;  // P = 0
-          dp[r] = 0.f;        // dS = 0 * (0 - D) = 0 whatever the row data holds
+          dp[r] = 0.f;        // dS = 0 * 0 = 0 whatever the row data holds
         }
       }
     }
     const int tdO = tQ + T::BYTES, h = b & 1;
-    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][D x 64]
-    auto read_stats = [&](f32x4& L, f32x4& Dv, int rb) __attribute__((always_inline)) {
+    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][-D x 64]
+    auto read_stats = [&](f32x4& L, int rb) __attribute__((always_inline)) {
       L = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
-      Dv = *(const f32x4*)(stats + BT + 32 * h + 8 * rb + 4 * hf);
     };
+    // -D of block b + 1's queries in accumulator order (element r: query
+    // (r%4) + 8(r/4) + 4hf of the block): the starting value of its dP
+    const f32x16 nd_n = neg_d(b & 1 ? tQ2 : tQ, (b + 1) & 1);
     // Eight groups: the two score MFMAs of head-dim chunk j for block b + 1,
     // then P and dS of elements 2j, 2j + 1 of block b. The LSE / D values are
     // read one group pair ahead and the transposed fragments of the first 16
     // queries during the second half; the fences keep this order and the
     // register pressure of source order.
-    f32x4 L4[2], D4[2];
+    f32x4 L4[2];
     bf16x8 tq[T::NDB], td[T::NDB];  // transposed fragments of one 16-query half (kc)
     bf16x8 pb[2], sb[2];
-    read_stats(L4[0], D4[0], 0);
+    read_stats(L4[0], 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int rb = j >> 1, e = 2 * (j & 1), r = 2 * j;
-      if ((j & 1) == 0 && rb < 3) read_stats(L4[(rb + 1) & 1], D4[(rb + 1) & 1], rb + 1);
+      if ((j & 1) == 0 && rb < 3) read_stats(L4[(rb + 1) & 1], rb + 1);
       if (j >= 8 - T::NDB) {
         const int db = j - (8 - T::NDB);
         td[db] = tr_frag(lds, tdO, tl, h, 0, db);
@@ -305,12 +323,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
       }
       if (j < T::NC) {
         sc_n = mfma32x32x16(rq_n[j], kT[j], j == 0 ? (f32x16){} : sc_n);
-        dp_n = mfma32x32x16(rd_n[j], vT[j], j == 0 ? (f32x16){} : dp_n);
+        dp_n = mfma32x32x16(rd_n[j], vT[j], j == 0 ? nd_n : dp_n);
       }
-      const f32x4 L = L4[rb & 1], Dv = D4[rb & 1];
+      const f32x4 L = L4[rb & 1];
       const float p0 = fast_exp2(fmaf(sc[r], c2, -L[e]));
       const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
-      const float d0 = p0 * (dp[r] - Dv[e]), d1 = p1 * (dp[r + 1] - Dv[e + 1]);
+      const float d0 = p0 * dp[r], d1 = p1 * dp[r + 1];  // dp already holds dP - D
       const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
       pb[r >> 3][r & 7] = pp[0];
       pb[r >> 3][(r & 7) + 1] = pp[1];
@@ -353,7 +371,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   f32x16 scA, dpA, scB, dpB;
   bf16x8 rqA[T::NC], rdA[T::NC], rqB[T::NC], rdB[T::NC];
   read_rows(rqA, rdA, 0, 0);
-  score(scA, dpA, rqA, rdA);
+  score(scA, dpA, rqA, rdA, neg_d(0, 0));
   read_rows(rqB, rdB, 0, 1);
   // tile t in ring slot s (= t % 3); the next tile in s1, the copy target s2
   auto tile = [&](int t, int s, int s1, int s2) __attribute__((always_inline)) {
@@ -422,7 +440,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
     }
   }
   const float lq2 = qrow < N ? lse2[(size_t)bh * Npad + qrow] : 0.f;
-  const float dq_d = qrow < N ? Dsum[(size_t)bh * Npad + qrow] : 0.f;
+  // -D of this lane's query, the starting value of every dP^T accumulation
+  // (so the MFMA result is dP - D)
+  const float nd = qrow < N ? Dsum[(size_t)bh * Npad + qrow] : 0.f;
+  f32x16 nd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd16[r] = nd;
   f32x16 dqT[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) dqT[db] = (f32x16){};
@@ -471,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
     for (int h = 0; h < 2; ++h) {
       const int t = 2 * j + h;
       if (t >= n_st) continue;
-      f32x16 sT = (f32x16){}, dpT = (f32x16){};
+      f32x16 sT = (f32x16){}, dpT = nd16;
 #pragma unroll
       for (int c = 0; c < T::NC; ++c) {
         sT = mfma32x32x16(row_frag(lds, tK, tl, h, c), qT[c], sT);
@@ -495,7 +518,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
       for (int r = 0; r < 16; r += 2) {
         const float p0 = fast_exp2(fmaf(sT[r], c2, -lq2));
         const float p1 = fast_exp2(fmaf(sT[r + 1], c2, -lq2));
-        const bf16x2 ss = to_bf16x2(p0 * (dpT[r] - dq_d), p1 * (dpT[r + 1] - dq_d));
+        const bf16x2 ss = to_bf16x2(p0 * dpT[r], p1 * dpT[r + 1]);  // dpT holds dP - D
         sb[r >> 3][r & 7] = ss[0];
         sb[r >> 3][(r & 7) + 1] = ss[1];
       }
