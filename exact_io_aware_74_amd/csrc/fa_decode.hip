@@ -124,8 +124,10 @@ __device__ __forceinline__ void split_partial(const uint16_t* __restrict__ q, co
       const int key = base + T::G * u;
       if (key < kend) {
         const size_t off = rows.offset(u, key);
-        kk[u] = *(const u32x4*)(Kh + off);
-        vv[u] = *(const u32x4*)(Vh + off);
+        // non-temporal: every cached key is read once, so the stream is not
+        // kept in L2 or the Infinity Cache (measured 6.14 -> 6.59 TB/s)
+        kk[u] = __builtin_nontemporal_load((const u32x4*)(Kh + off));
+        vv[u] = __builtin_nontemporal_load((const u32x4*)(Vh + off));
       } else {
         kk[u] = (u32x4){};
         vv[u] = (u32x4){};
