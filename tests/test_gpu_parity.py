@@ -218,3 +218,18 @@ def test_extreme_logits():
     many times along a row."""
     q, k, v = si.random_case(41, 1, 2, 500, 64, "bf16", std=4.0)
     print("extreme", _fwd_case(q, k, v, "bf16", True, 1.0))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_rising_row_maxima(causal):
+    """Every row's logits climb along the keys (Q shifted along a unit direction u, K rows moved along u by a
+    ramp up to 100), so the reference maximum must be raised in many sub-tiles after the first, each time
+    rescaling an output that already holds earlier keys. A float64 model of the kernel's rule predicts the
+    exact update on about a third of all sub-tiles here (one 777-row head, d = 128); N is ragged."""
+    q, k, v = si.random_case(77, 1, 2, 777, 128, "bf16")
+    u = np.random.Generator(np.random.PCG64([0, 77])).standard_normal(128)
+    u /= np.linalg.norm(u)
+    ramp = np.linspace(0.0, 100.0, k.shape[2])[None, None, :, None]
+    q2 = si.f32_to_bf16_bits((si.as_float64(q, "bf16") + 3.0 * u).astype(np.float32))
+    k2 = si.f32_to_bf16_bits((si.as_float64(k, "bf16") + ramp * u).astype(np.float32))
+    print("rising", causal, _fwd_case(q2, k2, v, "bf16", causal, fa.default_scale(128)))
