@@ -307,7 +307,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps first; the clock takes about a dozen prefill+decode steps to settle")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="CPU work of the oracle baseline (0 disables it)")
     ap.add_argument("--bwd-steps", type=int, default=10,
