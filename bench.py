@@ -60,6 +60,17 @@ def measured_traffic(launches_per_record: int = 1):
     return rec.get("hbm_bytes_per_launch")
 
 
+def warm_up(torch, fn, min_ms: float = 30.0, min_calls: int = 2):
+    """Untimed calls of fn until about min_ms of GPU time has passed: after a change
+    of load the clock takes a few tens of milliseconds to settle."""
+    import time
+    t0, n = time.perf_counter(), 0
+    while n < min_calls or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def cpu_baseline(w, target_s: float):
     """The oracle, untuned, on whole heads of the prefill workload until about target_s seconds."""
     import numpy as np
@@ -104,8 +115,7 @@ def backward_leg(fa, torch, si, w, q, k, v, o, lse, steps):
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N) // 4, dtype=torch.float32, device=q.device)
     fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
     stream = torch.cuda.current_stream(q.device)
-    for _ in range(2):
-        fa.bwd(q, k, v, o, dout, lse, causal=True, scale=w.scale, out=grads, workspace=ws)
+    warm_up(torch, lambda: fa.bwd(q, k, v, o, dout, lse, causal=True, scale=w.scale, out=grads, workspace=ws))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
@@ -142,8 +152,7 @@ def paged_decode_leg(fa, torch, si, wd, dq, dk, dv, steps, page_size=16):
     lens = torch.full((B,), L, dtype=torch.int32, device=dq.device)
     out = torch.empty_like(dq)
     stream = torch.cuda.current_stream(dq.device)
-    for _ in range(2):
-        fa.decode_paged(dq, pools[0], pools[1], tab, lens, nsplit=wd.nsplit, out=out)
+    warm_up(torch, lambda: fa.decode_paged(dq, pools[0], pools[1], tab, lens, nsplit=wd.nsplit, out=out))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
@@ -173,8 +182,7 @@ def fp8_prefill_leg(fa, torch, si, w, steps):
     o = torch.empty(q.shape, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    for _ in range(3):
-        fa.fwd_fp8(q, k, v, ds, causal=True, scale=w.scale, out=o, lse=lse)
+    warm_up(torch, lambda: fa.fwd_fp8(q, k, v, ds, causal=True, scale=w.scale, out=o, lse=lse))
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     ev[0].record(stream)
@@ -235,8 +243,7 @@ def reported_configs_leg(fa, torch, si, wp, q, k, v, steps):
     stream = torch.cuda.current_stream()
 
     def timed(fn, n):
-        fn()
-        fn()
+        warm_up(torch, fn)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         torch.cuda.synchronize()
         ev[0].record(stream)
