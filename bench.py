@@ -9,8 +9,10 @@ stream around each call give the per-call kernel time.
 
 Prints one JSON line: `value` is the prefill's attention-forward throughput
 (algorithmic FLOPs / average prefill time), with a `roofline` entry for the
-fused kernel, the decode's HBM rate in `decode`, and the CPU oracle's
-throughput on a bounded sample of the prefill workload in `cpu_baseline`.
+fused kernel, the decode's HBM rate in `decode`, the CPU oracle's throughput
+on every head of the prefill workload in `cpu_baseline`, and in `parity` the
+whole-tensor comparison of the timed prefill and decode outputs with that
+oracle (the run exits non-zero if a bound fails).
 After the timed steps, the same decode over a paged cache (`paged_decode`),
 the backward pass on the prefill workload (`backward`), the other configurations
 of the plan (`reported_configs`: fp32 N=256, bf16 N=1024 d=64, 16K, and the
@@ -35,6 +37,7 @@ PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz (the pub
 PEAK_HBM_GBPS = 8000.0       # published HBM3E bandwidth
 PEAK_FP8_TFLOPS = 5033.2     # dense FP8 MFMA: twice the bf16 rate (the published 5.0 PFLOP/s)
 PEAK_FP32_TFLOPS = 157.3     # published fp32 rate (the fp32 forward is a VALU kernel; reported for information)
+BF16_REL_L2, BF16_MAX_ABS, BF16_LSE_ABS = 5e-3, 2e-2, 1e-3   # parity bounds on O (whole tensor) and LSE
 PREFILL = "bf16_h32_n8192_d128_causal_k2"
 DECODE = "decode_b16h32_l32768_d128"
 LONG = "bf16_b4h32_n131072_d128_causal"
@@ -71,39 +74,100 @@ def warm_up(torch, fn, min_ms: float = 30.0, min_calls: int = 2):
         n += 1
 
 
-def cpu_baseline(w, target_s: float):
-    """The oracle, untuned, on whole heads of the prefill workload until about target_s seconds."""
-    import numpy as np
-
-    import oracle
-    import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: report the affinity set
-        cores = len(os.sched_getaffinity(0))
-    heads, elapsed, flops = 0, 0.0, 0
-    while elapsed < target_s and heads < w.H:
-        h = heads
-        q, k, v = (si.as_float64(si.tensor_slice(w, t, 0, h), w.dtype)[None, None] for t in ("q", "k", "v"))
-        t0 = time.perf_counter()
-        O, _ = oracle.attention(q, k, v, w.causal, w.scale)
-        elapsed += time.perf_counter() - t0
-        assert np.isfinite(O).all()
-        flops += oracle.attention_flops(1, 1, w.N, w.d, w.causal)
-        heads += 1
-    cpu_model = "unknown"
+def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "cpu_model": cpu_model,
-            "sample": f"{heads} of {w.H} heads of the N=8192 d=128 causal prefill (all rows), fp64 numpy, "
-                      f"{elapsed:.1f} s"}
+    return "unknown"
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report the affinity set
+        return len(os.sched_getaffinity(0))
+
+
+class _Parity:
+    """Whole-tensor comparison accumulated head by head: relative L2 over every element, max abs
+    error, max LSE error and the worst head's relative L2."""
+
+    def __init__(self):
+        self.err2 = self.ref2 = self.max_abs = self.lse_abs = self.worst = 0.0
+        self.worst_head = None
+        self.heads = 0
+        self.finite = True
+
+    def add(self, key, got, ref, got_lse=None, ref_lse=None):
+        import numpy as np
+        got = np.asarray(got, np.float64)
+        diff = got - ref
+        e2, r2 = float(np.sum(diff * diff)), float(np.sum(ref * ref))
+        self.err2, self.ref2 = self.err2 + e2, self.ref2 + r2
+        self.max_abs = max(self.max_abs, float(np.abs(diff).max()))
+        self.finite = self.finite and bool(np.isfinite(got).all())
+        if r2 > 0 and (e2 / r2) ** 0.5 >= self.worst:
+            self.worst, self.worst_head = (e2 / r2) ** 0.5, key
+        if got_lse is not None:
+            self.lse_abs = max(self.lse_abs, float(np.abs(np.asarray(got_lse, np.float64) - ref_lse).max()))
+            self.finite = self.finite and bool(np.isfinite(got_lse).all())
+        self.heads += 1
+
+    def report(self, with_lse: bool):
+        rel = (self.err2 / self.ref2) ** 0.5
+        ok = self.finite and rel <= BF16_REL_L2 and self.max_abs <= BF16_MAX_ABS and (
+            not with_lse or self.lse_abs <= BF16_LSE_ABS)
+        r = {"heads": self.heads, "rel_l2": float(f"{rel:.4e}"), "max_abs": float(f"{self.max_abs:.4e}"),
+             "worst_head_rel_l2": float(f"{self.worst:.4e}"), "worst_head": list(self.worst_head), "pass": ok}
+        if with_lse:
+            r["lse_max_abs"] = float(f"{self.lse_abs:.4e}")
+        return r
+
+
+def cpu_oracle_leg(wp, o_gpu, lse_gpu, wd, dq_h, dk_h, dv_h, do_gpu):
+    """The oracle (untuned, serial, fp64 numpy) on every head of the prefill workload: its time is
+    the CPU baseline, and its O and LSE are compared with the timed GPU output over the whole
+    tensor. Then the decode workload's every head against the decode oracle (compared only; not
+    part of the CPU baseline's time)."""
+    import oracle
+    import seeded_inputs as si
+    pre = _Parity()
+    elapsed, flops = 0.0, 0
+    for h in range(wp.H):
+        q, k, v = (si.as_float64(si.tensor_slice(wp, t, 0, h), wp.dtype)[None, None] for t in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        O, L = oracle.attention(q, k, v, wp.causal, wp.scale)
+        elapsed += time.perf_counter() - t0
+        flops += oracle.attention_flops(1, 1, wp.N, wp.d, wp.causal)
+        pre.add((0, h), o_gpu[0, h], O[0, 0], lse_gpu[0, h], L[0, 0])
+    base = {"value": round(flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"all {wp.H} heads of the N=8192 d=128 causal prefill (all rows), fp64 numpy, one head at a "
+                      f"time, {elapsed:.1f} s"}
+
+    dec = _Parity()
+    t0 = time.perf_counter()
+
+    def one(bh):
+        b, h = bh
+        o, _ = oracle.decode(*(si.as_float64(x[b:b + 1, h:h + 1], wd.dtype) for x in (dq_h, dk_h, dv_h)))
+        return bh, o[0, 0]
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(min(8, len(os.sched_getaffinity(0)))) as ex:
+        for (b, h), ref in ex.map(one, [(b, h) for b in range(wd.B) for h in range(wd.H)]):
+            dec.add((b, h), do_gpu[b, h], ref)
+    parity = {"prefill": dict(pre.report(True), workload="B=1 H=32 N=8192 d=128 causal K x2, the timed output"),
+              "decode": dict(dec.report(False), workload="B=16 H=32 Lkv=32768 d=128 nsplit=64, the timed output",
+                             oracle_s=round(time.perf_counter() - t0, 1)),
+              "bounds": {"rel_l2": BF16_REL_L2, "max_abs": BF16_MAX_ABS, "lse_max_abs": BF16_LSE_ABS},
+              "reference": "the fp64 oracle (plain definition, S and P materialised), every element"}
+    parity["pass"] = parity["prefill"]["pass"] and parity["decode"]["pass"]
+    return base, parity
 
 
 def backward_leg(fa, torch, si, w, q, k, v, o, lse, steps):
@@ -310,14 +374,137 @@ def reported_configs_leg(fa, torch, si, wp, q, k, v, steps):
     return res
 
 
+ABLATION_WORKLOADS = {"n1024": "bf16_b4h16_n1024_d64_causal", "n8192": PREFILL}
+
+
+def ablation_profile_leg(fa, torch, si, label, calls):
+    """Only the fused forward and the three-kernel ablation (S and P through HBM) on one workload,
+    `calls` times each after one untimed call: the run the HBM byte counters are taken on."""
+    import numpy as np
+    w = si.WORKLOADS[ABLATION_WORKLOADS[label]]
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(si.tensor_full(w, t)).view(np.int16)).view(torch.bfloat16).cuda()
+               for t in ("q", "k", "v"))
+    ws = torch.empty(fa.naive_workspace_bytes(w.B, w.H, w.N) // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, fn in (("fused", lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale)),
+                     ("naive", lambda: fa.naive_fwd(q, k, v, causal=w.causal, scale=w.scale, workspace=ws))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        torch.cuda.synchronize()
+        res[name + "_ms"] = round((time.perf_counter() - t0) * 1e3 / calls, 3)
+    return {"leg": "ablation_profile", "workload": w.name, "calls": calls, **res}
+
+
+def _short_kernel(name: str) -> str:
+    name = name.strip('"').replace("(anonymous namespace)", "anon")
+    if name.startswith("void "):
+        name = name[5:]
+    depth, out = 0, []
+    for ch in name:              # drop the argument list, keep template arguments
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).replace("fa::", "")
+
+
+def _read_counter_csvs(path):
+    """{dispatch id: (kernel, grid, {counter: value})} from every *_counter_collection.csv under path."""
+    import csv
+    import glob
+    out = {}
+    for f in sorted(glob.glob(os.path.join(path, "**", "*_counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            key = (f, int(r["Dispatch_Id"]))
+            ent = out.setdefault(key, (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), {}))
+            ent[2][r["Counter_Name"]] = ent[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_counters(root: str, write_traffic: bool) -> str:
+    """Markdown table of FETCH_SIZE / WRITE_SIZE per kernel and grid from the counter runs under
+    root/<label>_fetch and root/<label>_write (label: n1024 or n8192). Each run's plain 1 GiB device
+    copy (bench.py --copy-calibration) calibrates its counter: bytes = counter KiB x 1024 x
+    (1 GiB / the copy's reading)."""
+    import seeded_inputs as si
+    lines, traffic = [], None
+    for label in sorted(ABLATION_WORKLOADS):
+        w = si.WORKLOADS[ABLATION_WORKLOADS[label]]
+        per = {}
+        scale = {}
+        for counter, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            d = os.path.join(root, f"{label}_{sub}")
+            if not os.path.isdir(d):
+                continue
+            disp = _read_counter_csvs(d)
+            copies = [c[counter] for k, g, c in disp.values() if "copyBuffer" in k and counter in c]
+            if not copies:
+                raise SystemExit(f"{d}: no calibration copy dispatch (run with --copy-calibration)")
+            scale[counter] = 1048576.0 / max(copies)
+            for k, g, c in disp.values():
+                if k.startswith(("fwd_bf16_kernel", "naive_")) and counter in c:
+                    per.setdefault((k, g), {}).setdefault(counter, []).append(c[counter])
+        if not per:
+            continue
+        comp = 4 * w.B * w.H * w.N * w.d * 2 + w.B * w.H * w.N * 4
+        sp = 4 * w.B * w.H * w.N * w.N * 4
+        lines += [f"### {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} bf16 causal", "",
+                  f"Calibration (1 GiB copy): FETCH_SIZE x {scale.get('FETCH_SIZE', float('nan')):.4f}, "
+                  f"WRITE_SIZE x {scale.get('WRITE_SIZE', float('nan')):.4f}.", "",
+                  "| kernel | grid (threads) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | write bytes "
+                  "| HBM bytes |", "|---|---|---|---|---|---|---|---|"]
+        tot = {"fused": 0.0, "naive": 0.0}
+        for (k, g), c in sorted(per.items()):
+            f = sum(c.get("FETCH_SIZE", [0])) / max(1, len(c.get("FETCH_SIZE", [])))
+            wv = sum(c.get("WRITE_SIZE", [0])) / max(1, len(c.get("WRITE_SIZE", [])))
+            rb, wb = f * 1024 * scale.get("FETCH_SIZE", 0), wv * 1024 * scale.get("WRITE_SIZE", 0)
+            tot["naive" if k.startswith("naive_") else "fused"] += rb + wb
+            n = max(len(v) for v in c.values())
+            lines.append(f"| `{k}` | {g} | {n} | {f:.1f} | {wv:.1f} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} |")
+            if write_traffic and label == "n8192" and k.startswith("fwd_bf16_kernel"):
+                traffic = {"kernel": k, "workload": "B=1 H=32 N=8192 d=128 bf16 causal",
+                           "kernel_source_digest": fwd_source_digest(), "read_bytes_per_launch": int(rb),
+                           "write_bytes_per_launch": int(wb), "hbm_bytes_per_launch": int(rb + wb),
+                           "fetch_scale": round(scale["FETCH_SIZE"], 4), "write_scale": round(scale["WRITE_SIZE"], 4),
+                           "summary": "profiles/ablation_vs_fused_hbm_bytes.md"}
+        lines += ["", f"Per call: fused kernel {tot['fused']:.4g} B of HBM traffic against {comp:,} compulsory "
+                      f"(Q, K, V, O, LSE); three-kernel ablation {tot['naive']:.4g} B, of which the S/P round trips "
+                      f"are {sp:,} B by the byte model (four fp32 passes over B*H*N*N). Measured ratio "
+                      f"naive / fused = {tot['naive'] / max(tot['fused'], 1):.1f}.", ""]
+    if traffic is not None:
+        with open(TRAFFIC_RECORD, "w") as fh:
+            json.dump(traffic, fh, indent=1)
+            fh.write("\n")
+    return "\n".join(lines)
+
+
+def summarize_stats(csv_path: str) -> str:
+    """Markdown table (kernel, grid, dispatches, avg/min/max us) from a rocprofv3 kernel trace CSV."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        per.setdefault((_short_kernel(r["Kernel_Name"]), g), []).append(dt)
+    lines = ["| kernel | grid (threads) | dispatches | avg us | min us | max us |", "|---|---|---|---|---|---|"]
+    for (k, g), ts in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {g} | {len(ts)} | {sum(ts) / len(ts):.1f} | {min(ts):.1f} | {max(ts):.1f} |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first; the clock takes about a dozen prefill+decode steps to settle")
-    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
-                    help="CPU work of the oracle baseline (0 disables it)")
+    ap.add_argument("--skip-oracle", action="store_true",
+                    help="skip the CPU oracle leg (the CPU baseline and the whole-tensor parity of the timed "
+                         "outputs); for profiler runs")
     ap.add_argument("--bwd-steps", type=int, default=10,
                     help="timed calls of the backward pass (reported apart from the step; 0 disables it)")
     ap.add_argument("--paged-steps", type=int, default=20,
@@ -331,7 +518,25 @@ def main():
                          "reported apart; 0 disables them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy (a reference for byte counters)")
+    ap.add_argument("--only", choices=sorted(ABLATION_WORKLOADS), default=None,
+                    help="run only the fused forward and the three-kernel ablation on this workload (n1024: "
+                         "B=4 H=16 N=1024 d=64; n8192: the prefill workload), --report-steps calls each; for the "
+                         "HBM byte counter runs")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="no GPU: print the markdown byte table of the FETCH_SIZE / WRITE_SIZE runs under "
+                         "DIR/<n1024|n8192>_<fetch|write>")
+    ap.add_argument("--write-traffic-record", action="store_true",
+                    help="with --summarize-counters: also write the fused 8K kernel's bytes per launch to "
+                         "profiles/traffic_fwd_bf16_n8192.json (with the current kernel source digest)")
+    ap.add_argument("--summarize-stats", metavar="CSV", default=None,
+                    help="no GPU: print the markdown table of a rocprofv3 kernel trace CSV")
     args = ap.parse_args()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, args.write_traffic_record))
+        return
+    if args.summarize_stats:
+        print(summarize_stats(args.summarize_stats))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
@@ -349,26 +554,30 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    def to_dev(x):
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
-    t_gen = time.perf_counter()
-    q, k, v = (to_dev(si.tensor_full(wp, t)) for t in ("q", "k", "v"))
-    dq = to_dev(si.tensor_full(wd, "q")[:, :, 0, :])
-    dk = to_dev(si.tensor_full(wd, "k"))
-    dv = to_dev(si.tensor_full(wd, "v"))
-    gen_s = time.perf_counter() - t_gen
-    o = torch.empty_like(q)
-    lse = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
-    do = torch.empty_like(dq)
-
     if args.copy_calibration:
         src = torch.ones(1 << 29, dtype=torch.int16, device=dev)    # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.only:
+        print(json.dumps(ablation_profile_leg(fa, torch, si, args.only, max(1, args.report_steps))), flush=True)
+        return
+
+    def to_dev(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    wp, wd = si.WORKLOADS[PREFILL], si.WORKLOADS[DECODE]
+    t_gen = time.perf_counter()
+    q, k, v = (to_dev(si.tensor_full(wp, t)) for t in ("q", "k", "v"))
+    dec_host = (si.tensor_full(wd, "q")[:, :, 0, :], si.tensor_full(wd, "k"), si.tensor_full(wd, "v"))
+    dq, dk, dv = (to_dev(x) for x in dec_host)
+    if args.skip_oracle:
+        del dec_host
+    gen_s = time.perf_counter() - t_gen
+    o = torch.empty_like(q)
+    lse = torch.empty((wp.B, wp.H, wp.N), dtype=torch.float32, device=dev)
+    do = torch.empty_like(dq)
 
     stream = torch.cuda.current_stream(dev)
 
@@ -393,6 +602,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert torch.isfinite(o).all().item() and torch.isfinite(do.float()).all().item()
+    if not args.skip_oracle:   # the timed outputs, for the whole-tensor comparison with the oracle
+        o_host, lse_host, do_host = o.float().cpu().numpy(), lse.cpu().numpy(), do.float().cpu().numpy()
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
@@ -447,9 +658,14 @@ def main():
         rec["fp8_prefill"] = fp8_prefill_leg(fa, torch, si, wp, args.fp8_steps)
     if args.long_steps > 0:
         rec["long_prefill"] = long_prefill_leg(fa, torch, si, args.long_steps)
-    if args.cpu_baseline_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(wp, args.cpu_baseline_seconds)
+    parity_ok = True
+    if not args.skip_oracle:
+        rec["cpu_baseline"], rec["parity"] = cpu_oracle_leg(wp, o_host, lse_host, wd, *dec_host, do_host)
+        parity_ok = rec["parity"]["pass"]
     print(json.dumps(rec), flush=True)
+    if not parity_ok:
+        print("parity with the oracle FAILED: " + json.dumps(rec["parity"]), file=sys.stderr, flush=True)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

@@ -124,10 +124,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
                                                        const float* __restrict__ LSE, float* __restrict__ lse2,
                                                        float* __restrict__ Dsum, int BH, int N, int Npad) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
-  const int gid = blockIdx.x * 256 + threadIdx.x;
-  const int prow = gid / LPR, part = gid % LPR;  // padded row index over BH * Npad
-  const int bh = prow / Npad, i = prow % Npad;
-  const bool valid = bh < BH && i < N;
+  // 64-bit: BH * Npad * LPR threads may pass 2^31
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t prow = gid / LPR;  // padded row index over BH * Npad
+  const int part = (int)(gid % LPR);
+  const size_t bh = prow / (size_t)Npad;
+  const int i = (int)(prow % (size_t)Npad);
+  const bool valid = bh < (size_t)BH && i < N;
   float acc = 0.f;
   if (valid) {
     const size_t off = ((size_t)bh * N + i) * D + 8 * part;
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (part == 0 && bh < BH) {
+  if (part == 0 && bh < (size_t)BH) {
     lse2[prow] = valid ? LSE[(size_t)bh * N + i] * kLog2e : 0.f;
     Dsum[prow] = valid ? -acc : 0.f;  // stored negated: the dP accumulations start from it
   }

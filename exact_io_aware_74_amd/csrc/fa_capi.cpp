@@ -201,7 +201,7 @@ int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, con
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
-  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  if (B <= 0 || H <= 0 || N <= 0 || N > INT_MAX - 64) return 0;
   return 2 * (size_t)B * (size_t)H * (size_t)fa::bwd_rows_padded(N) * sizeof(float);
 }
 
@@ -215,6 +215,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return FA_ERR_INVALID_ARG;
   const size_t need = fa_bwd_workspace_bytes(B, H, N);
   if (need == 0 || workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  // the statistics kernel runs d/8 lanes per padded row: its grid must fit
+  const int64_t prep_blocks = ((int64_t)B * H * fa::bwd_rows_padded(N) * (d / 8) + 255) / 256;
+  if (prep_blocks > INT_MAX) return FA_ERR_INVALID_ARG;
   const size_t bytes = (size_t)B * H * (size_t)N * (size_t)d * 2, lbytes = (size_t)B * H * (size_t)N * 4;
   const void* ins[] = {q, k, v, o, dout};
   void* outs[] = {dq, dk, dv};

@@ -3,6 +3,11 @@
 // Every call passes fake, never-dereferenced "device" addresses and at least
 // one invalid argument, or an empty problem, so validation must return before
 // any HIP call; the launchers are stubs that abort if reached.
+//
+// The few HIP runtime functions the C ABI calls are defined here too (the
+// driver links no HIP library), so the decode workspace's allocation can be
+// made to fail on demand: that path must return FA_ERR_NOMEM with nothing
+// launched, and a later growth must release the old buffer exactly once.
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -12,7 +17,38 @@
 #include "fa.h"
 #include "fa_launch.h"
 
+// ---- stand-ins for the HIP runtime calls of the C ABI ----
+static bool g_malloc_fails = false;
+static int g_mallocs = 0, g_frees = 0, g_syncs = 0;
+static uintptr_t g_next_fake = (uintptr_t)1 << 44;
+extern "C" {
+hipError_t hipGetDevice(int* dev) {
+  *dev = 0;
+  return hipSuccess;
+}
+hipError_t hipSetDevice(int) { return hipSuccess; }
+hipError_t hipGetLastError(void) { return hipSuccess; }
+hipError_t hipStreamSynchronize(hipStream_t) {
+  ++g_syncs;
+  return hipSuccess;
+}
+hipError_t hipMalloc(void** p, size_t bytes) {
+  if (g_malloc_fails) return hipErrorOutOfMemory;
+  ++g_mallocs;
+  *p = (void*)g_next_fake;
+  g_next_fake += (bytes + 0xFFFFF) & ~(uintptr_t)0xFFFFF;
+  return hipSuccess;
+}
+hipError_t hipFree(void* p) {
+  if (p) ++g_frees;
+  return hipSuccess;
+}
+}
+
 namespace fa {
+static bool g_decode_may_launch = false;
+static int g_decode_launches = 0;
+static float* g_last_ws = nullptr;
 [[noreturn]] static void reached(const char* what) {
   std::fprintf(stderr, "launcher %s reached from a call that should have failed validation\n", what);
   std::abort();
@@ -23,8 +59,13 @@ hipError_t launch_fwd_f32(const float*, const float*, const float*, float*, floa
                           hipStream_t) { reached("fwd_f32"); }
 hipError_t launch_fwd_fp8(const void*, const void*, const void*, void*, float*, int, int, int, int, bool, float,
                           float, float, float, hipStream_t) { reached("fwd_fp8"); }
-hipError_t launch_decode(const void*, const void*, const void*, void*, float*, int, int, int, int, int, int,
-                         hipStream_t) { reached("decode"); }
+hipError_t launch_decode(const void*, const void*, const void*, void*, float* ws, int, int, int, int, int, int,
+                         hipStream_t) {
+  if (!g_decode_may_launch) reached("decode");
+  ++g_decode_launches;
+  g_last_ws = ws;
+  return hipSuccess;
+}
 hipError_t launch_decode_paged(const void*, const void*, const void*, const int*, const int*, void*, float*, int, int,
                                int, int, int, int, int, int, hipStream_t) { reached("decode_paged"); }
 // the backward workspace rows: N rounded up to a multiple of 64 (the documented size)
@@ -142,6 +183,53 @@ int main() {
   EXPECT(fa_bwd(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 2, 100, 128, 1,
                 0.1f, nullptr, 0, nullptr),
          FA_OK);
+
+  // the backward's row-statistics grid (d/8 lanes per padded row) past 2^31 - 1 workgroups, with
+  // B*H*ceil(N/64) still inside an int; tensors 2^43 bytes apart so that nothing overlaps
+  {
+    const uintptr_t g = (uintptr_t)1 << 43;
+    auto P = [&](int i) { return (void*)(g * (uintptr_t)(i + 1)); };
+    const int Hb = 1 << 16, Nb = 1 << 20;
+    EXPECT(fa_bwd(P(0), P(1), P(2), P(3), P(4), (const float*)P(5), P(6), P(7), P(8), 1, Hb, Nb, 64, 1, 0.1f, P(9),
+                  fa_bwd_workspace_bytes(1, Hb, Nb), nullptr),
+           INV);
+    EXPECT((int)(fa_bwd_workspace_bytes(1, 1, 2147483647) == 0), 1);
+  }
+
+  // forced allocation failure of the decode workspace: FA_ERR_NOMEM, nothing launched
+  // (q, caches and o 2^40 bytes apart, so that larger caches do not overlap)
+  void* QF = (void*)((uintptr_t)1 << 40);
+  void* KF = (void*)((uintptr_t)2 << 40);
+  void* VF = (void*)((uintptr_t)3 << 40);
+  void* OF = (void*)((uintptr_t)4 << 40);
+  fa::g_decode_may_launch = true;
+  g_malloc_fails = true;
+  EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 100, 128, 4, nullptr), (int)FA_ERR_NOMEM);
+  EXPECT(fa_decode_paged(A, Bp, C, (const int32_t*)T, (const int32_t*)S, Dp, 2, 2, 128, 16, 8, 4, 4, nullptr),
+         (int)FA_ERR_NOMEM);
+  EXPECT(fa::g_decode_launches, 0);
+  EXPECT(g_mallocs, 0);
+  // a first buffer, then a growth whose allocation fails: the old buffer is released once (after
+  // the stream is synchronised) and nothing is launched; the next call allocates afresh
+  g_malloc_fails = false;
+  EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 100, 128, 4, nullptr), FA_OK);
+  EXPECT(fa::g_decode_launches, 1);
+  EXPECT(g_mallocs, 1);
+  g_malloc_fails = true;
+  EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 4000, 128, 64, nullptr), (int)FA_ERR_NOMEM);
+  EXPECT(fa::g_decode_launches, 1);
+  EXPECT(g_syncs, 1);
+  EXPECT(g_frees, 1);
+  EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 100, 128, 4, nullptr), (int)FA_ERR_NOMEM);  // nothing left to reuse
+  g_malloc_fails = false;
+  EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 100, 128, 4, nullptr), FA_OK);
+  EXPECT(fa::g_decode_launches, 2);
+  EXPECT(g_mallocs, 2);
+  fa_shutdown();
+  EXPECT(g_frees, 2);
+  fa_shutdown();  // twice: nothing left to free
+  EXPECT(g_frees, 2);
+  fa::g_decode_may_launch = false;
 
   const size_t nw = fa_naive_workspace_bytes(1, 1, 16);
   EXPECT(fa_naive_fwd(A, Bp, C, Dp, L, 1, 1, 16, 64, 0, 0.1f, W, nw - 4, nullptr), INV);

@@ -68,3 +68,55 @@ def sample_rows(N: int, count: int, seed: int, tile: int = 128):
     rng = np.random.default_rng(seed)
     rest = rng.choice(N, size=min(N, count), replace=False)
     return sorted(r for r in fixed.union(rest.tolist()) if 0 <= r < N)
+
+
+class WholeTensorCheck:
+    """Parity over a whole output tensor, accumulated head by head: relative L2 over every
+    element (sqrt of the summed squared errors over the summed squared reference), the
+    largest absolute error, the largest LSE error, and the worst head's relative L2."""
+
+    def __init__(self, dtype: str):
+        self.dtype = dtype
+        self.err2 = 0.0
+        self.ref2 = 0.0
+        self.max_abs = 0.0
+        self.lse_abs = 0.0
+        self.worst_head = (0.0, None)
+        self.heads = 0
+        self.finite = True
+
+    def add(self, key, got, ref, got_lse=None, ref_lse=None):
+        got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        self.finite = self.finite and bool(np.isfinite(got).all())
+        diff = got - ref
+        e2, r2 = float(np.sum(diff * diff)), float(np.sum(ref * ref))
+        self.err2 += e2
+        self.ref2 += r2
+        self.max_abs = max(self.max_abs, float(np.max(np.abs(diff))) if diff.size else 0.0)
+        head_rel = (e2 / r2) ** 0.5 if r2 > 0 else 0.0
+        if head_rel >= self.worst_head[0]:
+            self.worst_head = (head_rel, key)
+        if got_lse is not None:
+            gl = np.asarray(got_lse, np.float64)
+            self.finite = self.finite and bool(np.isfinite(gl).all())
+            self.lse_abs = max(self.lse_abs, float(np.max(np.abs(gl - np.asarray(ref_lse, np.float64)))))
+        self.heads += 1
+
+    @property
+    def rel_l2(self) -> float:
+        return (self.err2 / self.ref2) ** 0.5 if self.ref2 > 0 else 0.0
+
+    def summary(self) -> dict:
+        return {"heads": self.heads, "rel_l2": self.rel_l2, "max_abs": self.max_abs, "lse_max_abs": self.lse_abs,
+                "worst_head_rel_l2": self.worst_head[0], "worst_head": self.worst_head[1]}
+
+    def assert_bounds(self, with_lse: bool = True):
+        rel_b, abs_b, lse_b = ((BF16_REL_L2, BF16_MAX_ABS, BF16_LSE_ABS) if self.dtype == "bf16"
+                               else (F32_REL_L2, F32_MAX_ABS, F32_LSE_ABS))
+        s = self.summary()
+        assert self.finite, f"non-finite outputs: {s}"
+        assert self.rel_l2 <= rel_b, f"whole-tensor relative L2 {self.rel_l2:.3e} > {rel_b}: {s}"
+        assert self.max_abs <= abs_b, f"max abs {self.max_abs:.3e} > {abs_b}: {s}"
+        if with_lse:
+            assert self.lse_abs <= lse_b, f"LSE max abs {self.lse_abs:.3e} > {lse_b}: {s}"
+        return s

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
-              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode_paged", "fa_fwd_fp8"):
+              "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+              "fa_decode_paged", "fa_fwd_fp8"):
         assert n in names
     assert len(names) == len(set(names))
 
@@ -233,3 +234,18 @@ def test_bwd_validation(lib):
     assert bwd(lib, dk=0x600000) == INVALID      # dk aliases dout
     assert bwd(lib, ws=0x900000) == INVALID      # workspace aliases dv
     assert bwd(lib, B=0) == FA_OK and bwd(lib, N=0, ws=0, ws_bytes=0) == FA_OK   # empty problem: nothing enqueued
+
+
+def test_bwd_rejects_a_statistics_grid_past_int(lib):
+    """B*H*ceil(N/64) fits an int, but the row-statistics kernel's d/8 lanes per padded row would need
+    2^31 workgroups: rejected before any launch. The fake tensors sit 2^43 bytes apart, so nothing
+    overlaps and the grid check is what fails."""
+    H, N, d = 1 << 16, 1 << 20, 64
+    g = 1 << 43
+    ptr = [g * (i + 1) for i in range(10)]
+    ws_bytes = lib_ws = 2 * H * N * 4
+    assert bwd(lib, q=ptr[0], k=ptr[1], v=ptr[2], o=ptr[3], do=ptr[4], lse=ptr[5], dq=ptr[6], dk=ptr[7],
+               dv=ptr[8], ws=ptr[9], B=1, H=H, N=N, d=d, ws_bytes=ws_bytes) == INVALID
+    assert lib.fa_bwd_workspace_bytes(1, H, N) == lib_ws
+    assert lib.fa_bwd_workspace_bytes(1, 1, 2**31 - 1) == 0      # padding N to 64 rows would overflow
+

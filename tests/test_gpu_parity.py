@@ -10,7 +10,9 @@ import torch
 import oracle
 import seeded_inputs as si
 from exact_io_aware_74_amd import binding as fa
-from helpers import (assert_close, assert_lse_close, sample_rows, to_device, to_f64, workload_inputs)
+import oracle_pool
+from helpers import (WholeTensorCheck, assert_close, assert_lse_close, sample_rows, to_device, to_f64,
+                     workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,13 +51,28 @@ def test_workload_bf16_b4h16_n1024_d64_causal():
     print("bf16 4x16x1024x64 causal", _fwd_case(q, k, v, "bf16", w.causal, w.scale))
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["bf16_h32_n8192_d128_causal_k2", "bf16_h32_n16384_d128_causal"])
-def test_workload_long_prefill_sampled(name):
+def test_workload_whole_tensor(name):
+    """The 8K (K x2) and 16K causal prefills against the oracle on every element of O and LSE,
+    all 32 heads: whole-tensor relative L2, max abs and LSE bounds. The oracle runs head by head
+    in worker processes, each regenerating its head from the seed."""
     w = W[name]
     q, k, v = workload_inputs(w)
-    rows = sample_rows(w.N, 96, seed=w.wid)
-    heads = [(0, 0), (0, 7), (0, 19), (0, 31)]
-    print(name, _fwd_case(q, k, v, "bf16", w.causal, w.scale, rows=rows, heads=heads))
+    qd, kd, vd = (to_device(x, "bf16") for x in (q, k, v))
+    del q, k, v
+    o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    O = o.float().cpu().numpy()
+    L = lse.cpu().numpy()
+    del qd, kd, vd, o, lse
+    chk = WholeTensorCheck("bf16")
+    tasks = [(name, b, h) for b in range(w.B) for h in range(w.H)]
+    gib = 3.2 * w.N * w.N * 8 / 2**30          # about 3.2 score-sized float64 arrays live per task
+    for b, h, Oref, Lref in oracle_pool.run(oracle_pool.forward_head, tasks, oracle_pool.default_workers(gib)):
+        chk.add((b, h), O[b, h], Oref, L[b, h], Lref)
+    assert chk.heads == w.B * w.H
+    print(name, chk.assert_bounds())
 
 
 def test_workload_128k_prefill_sampled():
@@ -233,3 +250,58 @@ def test_rising_row_maxima(causal):
     q2 = si.f32_to_bf16_bits((si.as_float64(q, "bf16") + 3.0 * u).astype(np.float32))
     k2 = si.f32_to_bf16_bits((si.as_float64(k, "bf16") + ramp * u).astype(np.float32))
     print("rising", causal, _fwd_case(q2, k2, v, "bf16", causal, fa.default_scale(128)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_common_key_offset_shifts_only_lse(causal, d):
+    """Adding one vector u to every key row adds scale * q_i . u to every logit of row i: the softmax,
+    so O, is unchanged and the LSE moves by exactly that amount ("flashattention-memory-bound"
+    (appliedaiprep.com), "Exact or approximate? Exact"). K and u sit on a 1/16 grid with |K + u| < 8,
+    so K + u is exact in bf16 and the kernel sees precisely the shifted keys. Both runs are compared
+    with the oracle on the unshifted keys."""
+    B, H, N = 1, 3, 333
+    rng = np.random.Generator(np.random.PCG64([0, 9100, d, int(causal)]))
+    q = si.f32_to_bf16_bits(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    kq = np.clip(np.round(rng.standard_normal((B, H, N, d)) * 16), -64, 64) / 16          # |K| <= 4
+    u = np.clip(np.round(rng.standard_normal((B, H, 1, d)) * 24), -48, 48) / 16            # |u| <= 3
+    k = si.f32_to_bf16_bits(kq.astype(np.float32))
+    k_shift = si.f32_to_bf16_bits((kq + u).astype(np.float32))
+    assert np.array_equal(si.as_float64(k_shift, "bf16"), kq + u)                          # exact in bf16
+    v = si.f32_to_bf16_bits(rng.standard_normal((B, H, N, d), dtype=np.float32))
+    scale = fa.default_scale(d)
+    q64, v64 = si.as_float64(q, "bf16"), si.as_float64(v, "bf16")
+    Oref, Lref = oracle.attention(q64, kq, v64, causal, scale)
+    shift = float(np.float32(scale)) * np.einsum("bhnd,bhd->bhn", q64, u[:, :, 0, :])
+    qd, vd = to_device(q, "bf16"), to_device(v, "bf16")
+    o0, l0 = fa.fwd(qd, to_device(k, "bf16"), vd, causal=causal, scale=scale)
+    o1, l1 = fa.fwd(qd, to_device(k_shift, "bf16"), vd, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert_close(to_f64(o0), Oref, "bf16")
+    assert_lse_close(to_f64(l0), Lref, "bf16")
+    rel, mx = assert_close(to_f64(o1), Oref, "bf16", what="O with shifted keys")
+    lmx = assert_lse_close(to_f64(l1), Lref + shift, "bf16")
+    print("key offset", causal, d, rel, mx, lmx, float(np.abs(shift).max()))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_joint_key_value_permutation_and_query_permutation(d):
+    """Non-causal: permuting the K and V rows together leaves O and LSE unchanged, and permuting the
+    Q rows permutes them ("flashattention-memory-bound" (appliedaiprep.com), "Exact or approximate?
+    Exact"). The kernel's key order and wave membership change, so only rounding may differ:
+    every run is checked against the oracle on the original order."""
+    B, H, N = 2, 2, 450
+    q, k, v = si.random_case(9200 + d, B, H, N, d, "bf16", std=1.5)
+    scale = fa.default_scale(d)
+    Oref, Lref = oracle.attention(*(si.as_float64(x, "bf16") for x in (q, k, v)), False, scale)
+    pk = np.random.default_rng(d).permutation(N)
+    pq = np.random.default_rng(d + 1).permutation(N)
+    o1, l1 = fa.fwd(*(to_device(np.ascontiguousarray(x), "bf16") for x in (q, k[:, :, pk], v[:, :, pk])),
+                    causal=False, scale=scale)
+    o2, l2 = fa.fwd(*(to_device(np.ascontiguousarray(x), "bf16") for x in (q[:, :, pq], k, v)), causal=False,
+                    scale=scale)
+    torch.cuda.synchronize()
+    assert_close(to_f64(o1), Oref, "bf16", what="O with K/V rows permuted")
+    assert_lse_close(to_f64(l1), Lref, "bf16")
+    assert_close(to_f64(o2), Oref[:, :, pq], "bf16", what="O with Q rows permuted")
+    assert_lse_close(to_f64(l2), Lref[:, :, pq], "bf16")
