@@ -27,6 +27,7 @@ SIGNATURES = {
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _S, _P]),
     "fa_bwd_workspace_bytes": (_S, [_I, _I, _I]),
@@ -147,8 +148,11 @@ def fwd_fp8(q, k, v, descales, causal: bool = False, scale: float | None = None,
     return o, (lse if return_lse else None)
 
 
-def decode(q, kcache, vcache, nsplit: int = 64, out=None):
-    """Split-KV decode. q: [B,H,d] (or [B,H,1,d]) bf16; caches [B,H,Lkv,d] bf16. Returns o like q."""
+def decode(q, kcache, vcache, nsplit: int = 64, out=None, noalloc: bool = False):
+    """Split-KV decode. q: [B,H,d] (or [B,H,1,d]) bf16; caches [B,H,Lkv,d] bf16. Returns o like q.
+
+    noalloc=True calls fa_decode_noalloc (partials in the library's fixed per-device array; pass
+    ``out`` as well to allocate nothing at all)."""
     lib = load()
     q3 = q.reshape(q.shape[0], q.shape[1], q.shape[-1]) if q.dim() == 4 else q
     for name, t in (("q", q3), ("kcache", kcache), ("vcache", vcache)):
@@ -163,9 +167,10 @@ def decode(q, kcache, vcache, nsplit: int = 64, out=None):
     o = torch.empty_like(q) if out is None else out
     if o.numel() != q3.numel() or o.dtype != torch.bfloat16 or not o.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor like q")
+    fn = "fa_decode_noalloc" if noalloc else "fa_decode"
     with torch.cuda.device(q.device):
-        st = lib.fa_decode(_ptr(q3), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d, int(nsplit), _stream(q))
-    _check("fa_decode", st)
+        st = getattr(lib, fn)(_ptr(q3), _ptr(kcache), _ptr(vcache), _ptr(o), B, H, Lkv, d, int(nsplit), _stream(q))
+    _check(fn, st)
     return o
 
 

@@ -169,6 +169,29 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o, in
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* o, int B, int H, int Lkv, int d,
+                      int nsplit, void* stream) {
+  if (B < 0 || H < 0 || Lkv <= 0 || d <= 0 || nsplit <= 0) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0) return FA_OK;
+  if (!q || !kcache || !vcache || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  int chunk, ns;
+  decode_split_shape(Lkv, nsplit, &chunk, &ns);
+  const int64_t bh = (int64_t)B * H;
+  if (bh * ns > INT_MAX) return FA_ERR_INVALID_ARG;
+  const size_t qbytes = (size_t)bh * d * 2, cbytes = (size_t)bh * Lkv * d * 2;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, kcache, cbytes) || overlaps(o, qbytes, vcache, cbytes))
+    return FA_ERR_INVALID_ARG;
+  if (fa_decode_workspace_bytes(B, H, Lkv, d, nsplit) > FA_DECODE_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+
+  float* ws = nullptr;
+  hipError_t e = fa::decode_scratch(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  e = fa::launch_decode(q, kcache, vcache, o, ws, B, H, Lkv, d, ns, chunk, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
                     const int32_t* seq_lens, void* o, int B, int H, int d, int page_size, int num_pages,
                     int max_pages, int nsplit, void* stream) {
@@ -262,6 +285,7 @@ const char* fa_status_str(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
     case FA_ERR_HIP: return "FA_ERR_HIP";
     case FA_ERR_NOMEM: return "FA_ERR_NOMEM";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE";
     default: return "FA_ERR_UNKNOWN";
   }
 }

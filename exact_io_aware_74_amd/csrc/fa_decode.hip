@@ -16,6 +16,9 @@
 // (max, sum, output slice), and the groups are merged in LDS at the end.
 #include <float.h>
 
+#include <mutex>
+
+#include "fa.h"
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -289,6 +292,35 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o,
                          int d, int nsplit, int chunk, hipStream_t s) {
   if (d == 64) return launch_decode_t<64>(q, kc, vc, o, ws, B, H, Lkv, nsplit, chunk, s);
   return launch_decode_t<128>(q, kc, vc, o, ws, B, H, Lkv, nsplit, chunk, s);
+}
+
+// Decode partials in a fixed device array, for the entry point that allocates
+// nothing. Every GPU that loads the library holds its own copy until the
+// process ends. In host code `scratch` names a host-side stand-in, so its
+// device address is looked up once per device (with that device current) and
+// only that address is handed to kernels.
+static __device__ __align__(256) float scratch[FA_DECODE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = (float*)g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 template <int D>

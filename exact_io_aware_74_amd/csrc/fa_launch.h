@@ -22,6 +22,10 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, void* o, float* ws,
                          int B, int H, int Lkv, int d, int nsplit, int chunk, hipStream_t s);
 
+// The device address of this device's fixed decode-partials array
+// (FA_DECODE_SCRATCH_BYTES bytes), looked up on the first call per device.
+hipError_t decode_scratch(float** ptr);
+
 // Paged decode: pools [num_pages, H, 2^log2_page, d], table [B, max_pages],
 // lens [B] (device). Splits cover `chunk` keys of max_pages * 2^log2_page;
 // splits past a sequence's length are empty. `ws` as for launch_decode.

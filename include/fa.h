@@ -44,7 +44,8 @@ enum fa_status {
   FA_ERR_INVALID_ARG = -1, /* null or misaligned pointer, negative size, bad scale or nsplit */
   FA_ERR_UNSUPPORTED = -2, /* head dimension d other than 64 or 128 */
   FA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-  FA_ERR_NOMEM = -4        /* the library could not allocate its decode workspace */
+  FA_ERR_NOMEM = -4,       /* the library could not allocate its decode workspace */
+  FA_ERR_TOO_LARGE = -5    /* the problem needs more than the fixed FA_DECODE_SCRATCH_BYTES */
 };
 
 /*
@@ -130,6 +131,31 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, void* o,
 
 /* Bytes of decode partials for this shape (the buffer fa_decode keeps). */
 size_t fa_decode_workspace_bytes(int B, int H, int Lkv, int d, int nsplit);
+
+/* Size of the fixed per-device decode-partials array of fa_decode_noalloc. */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * fa_decode_noalloc -- fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. Same operation, arguments, layouts, kernels and
+ * results as fa_decode (bit for bit), but the partials live in a fixed
+ * device array of FA_DECODE_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it runs on until the process ends. The call never allocates,
+ * frees or synchronises; on its first call on a device it looks up that
+ * device's array address (no allocation).
+ *
+ * Limit: fa_decode_workspace_bytes(B, H, Lkv, d, nsplit) must not exceed
+ * FA_DECODE_SCRATCH_BYTES (32 MiB: e.g. B*H = 1024 heads at d = 128 with 64
+ * splits need 17,039,360 bytes), else FA_ERR_TOO_LARGE before anything is
+ * enqueued. Every call on one GPU shares that GPU's array, so calls that may
+ * overlap in time on one GPU (different streams without ordering between
+ * them) race: order them, or use fa_decode. Nothing in the array needs
+ * clearing: each split writes its whole partial before the merge reads it.
+ * Other errors as fa_decode (never FA_ERR_NOMEM).
+ */
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, void* o,
+                      int B, int H, int Lkv, int d, int nsplit, void* stream);
 
 /*
  * fa_decode_paged -- fa_decode over a paged KV cache: the keys of each

@@ -49,6 +49,7 @@ namespace fa {
 static bool g_decode_may_launch = false;
 static int g_decode_launches = 0;
 static float* g_last_ws = nullptr;
+static float* const kFakeScratch = (float*)((uintptr_t)1 << 45);
 [[noreturn]] static void reached(const char* what) {
   std::fprintf(stderr, "launcher %s reached from a call that should have failed validation\n", what);
   std::abort();
@@ -64,6 +65,11 @@ hipError_t launch_decode(const void*, const void*, const void*, void*, float* ws
   if (!g_decode_may_launch) reached("decode");
   ++g_decode_launches;
   g_last_ws = ws;
+  return hipSuccess;
+}
+hipError_t decode_scratch(float** ptr) {
+  if (!g_decode_may_launch) reached("decode_scratch");
+  *ptr = kFakeScratch;
   return hipSuccess;
 }
 hipError_t launch_decode_paged(const void*, const void*, const void*, const int*, const int*, void*, float*, int, int,
@@ -196,6 +202,20 @@ int main() {
     EXPECT((int)(fa_bwd_workspace_bytes(1, 1, 2147483647) == 0), 1);
   }
 
+  // fa_decode_noalloc: fa_decode's validation, then the fixed array's limit
+  EXPECT(fa_decode_noalloc(A, Bp, C, Dp, 2, 2, 100, 80, 4, nullptr), UNS);
+  EXPECT(fa_decode_noalloc(A, Bp, C, Dp, 2, 2, 0, 128, 4, nullptr), INV);
+  EXPECT(fa_decode_noalloc(nullptr, Bp, C, Dp, 2, 2, 100, 128, 4, nullptr), INV);
+  EXPECT(fa_decode_noalloc(A, Bp, off(C, 4), Dp, 2, 2, 100, 128, 4, nullptr), INV);
+  EXPECT(fa_decode_noalloc(A, Bp, C, Bp, 2, 2, 100, 128, 4, nullptr), INV);
+  EXPECT(fa_decode_noalloc(nullptr, nullptr, nullptr, nullptr, 0, 2, 100, 128, 4, nullptr), FA_OK);
+  {
+    // 64*32 heads, 64 splits, d = 128: 68,157,440 bytes of partials > 32 MiB (caches 2^40 bytes apart)
+    const uintptr_t g = (uintptr_t)1 << 40;
+    EXPECT(fa_decode_noalloc((void*)g, (void*)(2 * g), (void*)(3 * g), (void*)(4 * g), 64, 32, 64, 128, 64, nullptr),
+           (int)FA_ERR_TOO_LARGE);
+  }
+
   // forced allocation failure of the decode workspace: FA_ERR_NOMEM, nothing launched
   // (q, caches and o 2^40 bytes apart, so that larger caches do not overlap)
   void* QF = (void*)((uintptr_t)1 << 40);
@@ -225,6 +245,11 @@ int main() {
   EXPECT(fa_decode(QF, KF, VF, OF, 2, 2, 100, 128, 4, nullptr), FA_OK);
   EXPECT(fa::g_decode_launches, 2);
   EXPECT(g_mallocs, 2);
+  // the no-allocation entry point takes the fixed array and never allocates
+  EXPECT(fa_decode_noalloc(QF, KF, VF, OF, 16, 32, 32768, 128, 64, nullptr), FA_OK);
+  EXPECT(fa::g_decode_launches, 3);
+  EXPECT((int)(fa::g_last_ws == fa::kFakeScratch), 1);
+  EXPECT(g_mallocs, 2);
   fa_shutdown();
   EXPECT(g_frees, 2);
   fa_shutdown();  // twice: nothing left to free
@@ -243,7 +268,7 @@ int main() {
   EXPECT((int)(fa_bwd_workspace_bytes(1, 32, 8192) == 2u * 32 * 8192 * 4), 1);
   EXPECT((int)(fa_naive_workspace_bytes(1, 1, 0) == 0), 1);
   EXPECT((int)(fa_naive_workspace_bytes(4, 32, 131072) == (size_t)4 * 32 * 131072 * 131072 * 4), 1);
-  for (int st : {(int)FA_OK, INV, UNS, (int)FA_ERR_HIP, (int)FA_ERR_NOMEM, -99})
+  for (int st : {(int)FA_OK, INV, UNS, (int)FA_ERR_HIP, (int)FA_ERR_NOMEM, (int)FA_ERR_TOO_LARGE, -99})
     if (fa_status_str(st) == nullptr) ++failures;
 
   if (failures) {

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_str",
               "fa_last_hip_error", "fa_shutdown", "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
-              "fa_decode_paged", "fa_fwd_fp8"):
+              "fa_decode_paged", "fa_fwd_fp8", "fa_decode_noalloc"):
         assert n in names
     assert len(names) == len(set(names))
 
@@ -182,6 +182,7 @@ def test_status_strings(lib):
     assert lib.fa_status_str(-2) == b"FA_ERR_UNSUPPORTED"
     assert lib.fa_status_str(-3) == b"FA_ERR_HIP"
     assert lib.fa_status_str(-4) == b"FA_ERR_NOMEM"
+    assert lib.fa_status_str(-5) == b"FA_ERR_TOO_LARGE"
     assert lib.fa_status_str(7) == b"FA_ERR_UNKNOWN"
     assert lib.fa_last_hip_error() == 0
 
@@ -249,3 +250,17 @@ def test_bwd_rejects_a_statistics_grid_past_int(lib):
     assert lib.fa_bwd_workspace_bytes(1, H, N) == lib_ws
     assert lib.fa_bwd_workspace_bytes(1, 1, 2**31 - 1) == 0      # padding N to 64 rows would overflow
 
+
+def test_decode_noalloc_validation(lib):
+    """fa_decode's checks, then the fixed 32 MiB partials array's limit, all before any HIP call."""
+    g = 1 << 40   # fake tensors far apart: large caches do not overlap
+
+    def call(B=2, H=2, L=100, d=128, ns=4, q=g, k=2 * g, v=3 * g, o=4 * g):
+        return lib.fa_decode_noalloc(q, k, v, o, B, H, L, d, ns, None)
+    assert call(d=80) == UNSUPPORTED
+    assert call(L=0) == INVALID and call(ns=0) == INVALID and call(B=-1) == INVALID
+    assert call(q=0) == INVALID and call(v=3 * g + 4) == INVALID and call(o=2 * g) == INVALID
+    assert call(B=0, q=0, k=0, v=0, o=0) == FA_OK
+    assert lib.fa_decode_workspace_bytes(64, 32, 64, 128, 64) == 68157440 > 32 << 20
+    assert call(B=64, H=32, L=64, ns=64) == -5                         # FA_ERR_TOO_LARGE
+    assert lib.fa_decode_workspace_bytes(16, 32, 32768, 128, 64) <= 32 << 20   # the decode workload fits

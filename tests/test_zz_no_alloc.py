@@ -1,0 +1,70 @@
+"""fa_decode_noalloc: the split-KV decode with its partials in the library's fixed
+per-device array instead of an allocated workspace. Called through the C ABI and
+compared with fa_decode (the same kernels: bit for bit) and with the oracle, on two
+calls in a row, the second with a smaller input, with no change in device memory."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from exact_io_aware_74_amd import binding as fa
+from helpers import assert_close, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, H, L, d):
+    q, k, v = si.random_case(seed, B, H, 1, d, "bf16", nk=L, std=2.0)
+    dev = (to_device(q[:, :, 0, :], "bf16"), to_device(k, "bf16"), to_device(v, "bf16"))
+    ref, _ = oracle.decode(si.as_float64(q, "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
+    return dev, ref
+
+
+def test_noalloc_matches_decode_on_two_calls_in_a_row():
+    big, ref_big = _case(101, 4, 8, 3000, 128)      # 4*8*64*(128+2)*4 = 1,064,960 bytes of partials
+    small, ref_small = _case(102, 2, 3, 257, 64)     # then a smaller problem into the same array
+    out_big = torch.empty_like(big[0])
+    out_small = torch.empty_like(small[0])
+    # the first call on this device looks up the array's address (and loads the library's code)
+    fa.decode(*small, nsplit=7, out=out_small, noalloc=True)
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    fa.decode(*big, nsplit=64, out=out_big, noalloc=True)
+    fa.decode(*small, nsplit=7, out=out_small, noalloc=True)
+    torch.cuda.synchronize()
+    assert torch.cuda.mem_get_info()[0] == free0, "fa_decode_noalloc changed the device's free memory"
+    want_big = fa.decode(*big, nsplit=64)
+    want_small = fa.decode(*small, nsplit=7)
+    torch.cuda.synchronize()
+    assert torch.equal(out_big, want_big)
+    assert torch.equal(out_small, want_small)
+    assert_close(to_f64(out_big), ref_big, "bf16")
+    assert_close(to_f64(out_small), ref_small, "bf16")
+
+
+def test_noalloc_at_the_full_decode_workload_size():
+    """B=16 H=32 Lkv=32768 d=128 nsplit=64: 17,039,360 bytes of partials, inside the 32 MiB array;
+    equal to fa_decode on every head."""
+    w = si.WORKLOADS["decode_b16h32_l32768_d128"]
+    assert fa.decode_workspace_bytes(w.B, w.H, w.Lkv, w.d, w.nsplit) == 17039360
+    q = to_device(si.tensor_full(w, "q")[:, :, 0, :], "bf16")
+    k = to_device(si.tensor_full(w, "k"), "bf16")
+    v = to_device(si.tensor_full(w, "v"), "bf16")
+    got = fa.decode(q, k, v, nsplit=w.nsplit, noalloc=True)
+    want = fa.decode(q, k, v, nsplit=w.nsplit)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert torch.isfinite(got.float()).all().item()
+
+
+def test_noalloc_rejects_a_problem_past_the_array():
+    """64*32 heads at d = 128 with 64 splits need 68 MB of partials: FA_ERR_TOO_LARGE, nothing enqueued."""
+    q = torch.zeros((64, 32, 128), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((64, 32, 64, 128), dtype=torch.bfloat16, device="cuda")
+    o = torch.full_like(q, 3.0)
+    with pytest.raises(fa.FaError) as ei:
+        fa.decode(q, kc, kc, nsplit=64, out=o, noalloc=True)
+    assert ei.value.status == -5
+    torch.cuda.synchronize()
+    assert (o == 3.0).all().item()
