@@ -502,6 +502,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first; the clock takes about a dozen prefill+decode steps to settle")
+    ap.add_argument("--warmup-min-seconds", type=float, default=0.2,
+                    help="the untimed steps continue (past --warmup) until this much wall time has passed")
     ap.add_argument("--skip-oracle", action="store_true",
                     help="skip the CPU oracle leg (the CPU baseline and the whole-tensor parity of the timed "
                          "outputs); for profiler runs")
@@ -591,9 +593,13 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
-    for _ in range(args.warmup):
+    # W untimed steps, continued until the clock has settled: the GPU takes about a dozen prefill+decode
+    # steps (20-30 ms) to reach its steady clock under this load, so fewer steps would time the transient
+    t_w, n_warm = time.perf_counter(), 0
+    while n_warm < args.warmup or time.perf_counter() - t_w < args.warmup_min_seconds:
         step()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n_warm += 1
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -623,6 +629,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": n_warm,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -79,6 +79,8 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
                int causal, float scale, void* stream) {
   const int st = check_fwd(q, k, v, o, lse, B, H, N, d, scale, 4);
   if (st != FA_OK) return st == 1 ? FA_OK : st;
+  // the fp32 kernel runs one workgroup per four query rows: its grid must fit an int
+  if ((int64_t)B * H * (((int64_t)N + 3) / 4) > INT_MAX) return FA_ERR_INVALID_ARG;
   const hipError_t e = fa::launch_fwd_f32(q, k, v, o, lse, B, H, N, d, causal != 0, scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : hip_fail(e);
 }

@@ -50,26 +50,6 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS s16x4*)(p));
 }
 
-// O^T-style accumulation with the accumulator pinned in AGPRs. The compiler
-// does not see inside the asm, so the hazards it would otherwise pad are
-// handled here: `s_nop 1` gives the two wait states a VALU write of an
-// operand (the bf16 probabilities) needs before the matrix core reads it.
-// Back-to-back MFMAs on the same accumulator need no padding.
-__device__ __forceinline__ void mfma32x32x16_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Orders all later accesses to `acc` after this point and, with WAIT, first
-// gives the 19 wait states an MFMA result needs before VALU instructions
-// (v_accvgpr_read/write) may read or overwrite it.
-template <bool WAIT>
-__device__ __forceinline__ void agpr_fence(f32x16& acc) {
-  if constexpr (WAIT)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+a"(acc));
-  else
-    asm volatile("" : "+a"(acc));
-}
-
 // 16-byte copy global -> LDS without a VGPR round trip: lane l's 16 bytes
 // land at LDS byte address `lds_addr` + 16*l (`lds_addr` wave-uniform). Issued
 // through asm so the compiler does not tie later LDS reads to its completion

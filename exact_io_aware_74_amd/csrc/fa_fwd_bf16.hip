@@ -9,9 +9,10 @@
 // running row maximum is raised. The N x N score matrix never leaves the chip.
 //
 // Mapping onto CDNA4 (lane layouts in fa_device.h):
-//  * one workgroup = 8 waves (two per SIMD) x 32 query rows = 256 rows of one
-//    (b, h) head (the code also builds a 4-wave variant with 64 rows per
-//    wave, see kFwdQB);
+//  * one workgroup = NW waves x 32 query rows of one (b, h) head: 8 waves (256
+//    rows, two waves per SIMD) normally; 4 waves (128 rows, two workgroups per
+//    CU) at d = 64 when 256-row tiles would leave the chip short of
+//    workgroups, so the heaviest causal tile is half as long;
 //  * scores are computed transposed, S^T = K Q^T, with K rows as the A operand
 //    (LDS) and the wave's queries as the B operand (VGPRs, loaded once). In the
 //    accumulator lane l owns query l % 32 and 16 keys of a 32-key block, so row
@@ -50,10 +51,9 @@
 
 namespace fa {
 
-template <int D, int QB>
+template <int D, int NW>
 struct FwdTile {
-  static constexpr int NW = 8 / QB;             // waves per workgroup
-  static constexpr int WR = 32 * QB;            // query rows per wave (QB MFMA blocks of 32)
+  static constexpr int WR = 32;                 // query rows per wave (one MFMA block)
   static constexpr int BR = NW * WR;            // query rows per workgroup
   static constexpr int BC = 64;                 // keys per LDS tile (two 32-key sub-tiles)
   static constexpr int NBUF = 4;                // LDS ring depth
@@ -64,34 +64,10 @@ struct FwdTile {
   static constexpr int KT = BC * D * 2;         // bytes of one K (or V) tile: [octet][key][128 B]
   static constexpr int VREG = NBUF * KT;        // the V ring follows the K ring
   static constexpr int IPW = CH / NW;           // DMA instructions per wave per tensor per tile
+  static constexpr int WG_PER_CU = 8 / NW;      // workgroups per CU for two waves per SIMD
   static_assert(IPW * NW == CH, "DMA split");
-  static_assert(2 * NBUF * KT <= 163840, "LDS budget");
+  static_assert(WG_PER_CU * 2 * NBUF * KT <= 163840, "LDS budget");
 };
-
-// O^T += V^T P^T for one 32x32 block. With one query block per wave O^T
-// (64 registers at d = 128) lives in VGPRs next to everything else and the
-// compiler's MFMA is used; with two blocks O^T needs 128 registers and is
-// pinned in AGPRs through asm (the scores stay in VGPRs for the softmax).
-template <int QB>
-__device__ __forceinline__ void pv_mfma(f32x16& acc, const bf16x8& v, const bf16x8& p) {
-  if constexpr (QB == 1)
-    acc = mfma32x32x16(v, p, acc);
-  else
-    mfma32x32x16_agpr(acc, v, p);
-}
-// Makes the O^T accumulators safe to touch with VALU instructions (only the
-// AGPR variant needs the explicit wait states).
-template <int QB, int NDB>
-__device__ __forceinline__ void o_fence(f32x16 (&oacc)[QB][NDB]) {
-  if constexpr (QB > 1) {
-    agpr_fence<true>(oacc[0][0]);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        if (qb + db > 0) agpr_fence<false>(oacc[qb][db]);
-  }
-}
 
 // Largest in-lane sum of a sub-tile's probabilities accepted against the
 // current reference maximum. Probabilities are non-negative, so the sum bounds
@@ -109,13 +85,13 @@ constexpr float kPsumLimit = 256.f;
 __device__ __forceinline__ int swz_k(int key) { return (key >> 1) & 7; }
 __device__ __forceinline__ int swz_v(int key) { return 4 * ((key >> 1) & 1); }
 
-template <int D, int QB, bool CAUSAL>
-__global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
-                                                          const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V,
-                                                          uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                          int N, float scale, float c2, int n_qt, int BH) {
-  using T = FwdTile<D, QB>;
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                                   const uint16_t* __restrict__ K,
+                                                                   const uint16_t* __restrict__ V,
+                                                                   uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                                   int N, float scale, float c2, int n_qt, int BH) {
+  using T = FwdTile<D, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::NBUF * T::KT];
 
   const int tid = threadIdx.x;
@@ -130,6 +106,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
   const int wq0 = q0 + T::WR * w;  // first query row of this wave
+  const int qrow = wq0 + lq;       // the query row this lane's scores and output belong to
 
   // ---- DMA of one K/V tile into a ring slot: instruction v of the tile
   // (wave w issues v = w*IPW .. w*IPW + IPW - 1 for each tensor) copies octet
@@ -182,17 +159,13 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   if (n_kt > 1) dma(1, 1);
 
   // ---- Q^T as the B operand: k-slots of chunk c are head dims 16c + 8*hf + (0..7) ----
-  bf16x8 qop[QB][T::NC];
+  bf16x8 qop[T::NC];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wq0 + 32 * qb + lq;
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      if (row < N)
-        qop[qb][c] = *(const bf16x8*)(Qh + (size_t)row * D + 16 * c + 8 * hf);
-      else
-        qop[qb][c] = (bf16x8){};
-    }
+  for (int c = 0; c < T::NC; ++c) {
+    if (qrow < N)
+      qop[c] = *(const bf16x8*)(Qh + (size_t)qrow * D + 16 * c + 8 * hf);
+    else
+      qop[c] = (bf16x8){};
   }
 
   // Per-lane LDS byte offsets within a ring slot. K fragment (A operand of
@@ -213,18 +186,12 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     v_lane[a] = T::VREG + key * 128 + 16 * (chunk ^ swz_v(key)) + 8 * (s16 & 1);
   }
 
-  f32x16 sA[QB], sB[QB];    // S^T of one 32-key sub-tile per query block (VGPRs)
-  f32x16 oacc[QB][T::NDB];  // O^T (AGPRs): lane l owns query l % 32 of each block
-  float m[QB];              // reference maximum of the raw scores q.k
-  float lsum[QB];           // this half-wave's share of the running sum
-  float mt[QB];             // maximum of a sub-tile (exact update only)
+  f32x16 sA, sB;            // S^T of one 32-key sub-tile (VGPRs)
+  f32x16 oacc[T::NDB];      // O^T: lane l owns query l % 32
+  float m = -INFINITY;      // reference maximum of the raw scores q.k
+  float lsum = 0.f;         // this half-wave's share of the running sum
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-    for (int db = 0; db < T::NDB; ++db) oacc[qb][db] = (f32x16){};
-    m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-  }
+  for (int db = 0; db < T::NDB; ++db) oacc[db] = (f32x16){};
 
   // K fragment c (A operand of S^T) of 32-key half h of the tile in the ring
   // slot at byte offset k_slot
@@ -232,87 +199,64 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
     return *(const bf16x8*)(lds + (k_lane[c & 3] + k_slot) + ((c >> 2) * (T::BC * 128) + h * 32 * 128));
   };
   // S^T for the 32-key half h of the tile in the slot at k_slot
-  auto qk = [&](f32x16(&s)[QB], int k_slot, int h) __attribute__((always_inline)) {
+  auto qk = [&](f32x16& s, int k_slot, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      const bf16x8 a = k_frag(k_slot, h, c);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = mfma32x32x16(a, qop[qb][c], c == 0 ? (f32x16){} : s[qb]);
-    }
-  };
-  auto tile_max = [&](const f32x16(&s)[QB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float x = s[qb][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) x = fmaxf(x, s[qb][r]);
-      mt[qb] = halves_max(x);
-    }
+    for (int c = 0; c < T::NC; ++c) s = mfma32x32x16(k_frag(k_slot, h, c), qop[c], c == 0 ? (f32x16){} : s);
   };
   // keys past N and (causal) keys after the query row get -inf
   auto needs_mask = [&](int t) __attribute__((always_inline)) {
     return (32 * t + 32 > N) || (CAUSAL && 32 * t + 31 > wq0);
   };
-  auto mask = [&](f32x16(&s)[QB], int t) __attribute__((always_inline)) {
+  auto mask = [&](f32x16& s, int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = wq0 + 32 * qb + lq;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
-        const bool vis = key < N && (!CAUSAL || key <= qrow);
-        if (!vis) s[qb][r] = -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * t + (r & 3) + 8 * (r >> 2) + 4 * hf;
+      const bool vis = key < N && (!CAUSAL || key <= qrow);
+      if (!vis) s[r] = -INFINITY;
     }
   };
   // The exact online-softmax update for sub-tile s: the reference maximum
   // of every row becomes max(m, rowmax s) and O and the running sum are
   // rescaled by alpha = exp2((m_old - m_new) c2) (alpha = 1 where the
-  // maximum did not move). Returns alpha per query block.
-  auto raise_ref = [&](const f32x16(&s)[QB], float(&alpha)[QB]) __attribute__((always_inline)) {
-    tile_max(s);
-    o_fence(oacc);
+  // maximum did not move).
+  auto raise_ref = [&](const f32x16& s) __attribute__((always_inline)) {
+    float x = s[0];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_new = fmaxf(m[qb], mt[qb]);
-      alpha[qb] = fast_exp2((m[qb] - m_new) * c2);
-      m[qb] = m_new;
-      lsum[qb] *= alpha[qb];
+    for (int r = 1; r < 16; ++r) x = fmaxf(x, s[r]);
+    const float m_new = fmaxf(m, halves_max(x));
+    const float alpha = fast_exp2((m - m_new) * c2);
+    m = m_new;
+    lsum *= alpha;
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha[qb];
-    }
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
   };
   // True (wave-uniform) when some lane's probability sum is above the limit
   // or not finite.
-  auto over_limit = [&](const float(&x)[QB]) __attribute__((always_inline)) {
-    bool bad = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) bad = bad || !(x[qb] <= kPsumLimit);
-    return __builtin_expect(__builtin_amdgcn_ballot_w64(bad) != 0, 0);
+  auto over_limit = [&](float x) __attribute__((always_inline)) {
+    return __builtin_expect(__builtin_amdgcn_ballot_w64(!(x <= kPsumLimit)) != 0, 0);
   };
   // Probabilities of a sub-tile against the reference maximum: bf16 B operand
   // of P V and this half-wave's fp32 row sums. One call handles elements r,
-  // r + 1 of query block qb (mc = reference maximum in exp2 units).
-  // The sum goes to ps0 for the first 16-key chunk (elements 0-7) and to ps1
-  // for the second: two independent add chains.
-  auto prob_pair = [&](const f32x16(&s)[QB], bf16x8(&pb)[QB][2], float(&ps0)[QB], float(&ps1)[QB],
-                       const float(&mc)[QB], int qb, int r) __attribute__((always_inline)) {
-    const float p0 = fast_exp2(fmaf(s[qb][r], c2, -mc[qb]));
-    const float p1 = fast_exp2(fmaf(s[qb][r + 1], c2, -mc[qb]));
+  // r + 1 (mc = reference maximum in exp2 units). The sum goes to ps0 for the
+  // first 16-key chunk (elements 0-7) and to ps1 for the second: two
+  // independent add chains.
+  auto prob_pair = [&](const f32x16& s, bf16x8(&pb)[2], float& ps0, float& ps1, float mc, int r)
+                       __attribute__((always_inline)) {
+    const float p0 = fast_exp2(fmaf(s[r], c2, -mc));
+    const float p1 = fast_exp2(fmaf(s[r + 1], c2, -mc));
     if (r < 8)
-      ps0[qb] += p0 + p1;
+      ps0 += p0 + p1;
     else
-      ps1[qb] += p0 + p1;
+      ps1 += p0 + p1;
     const bf16x2 two = to_bf16x2(p0, p1);
-    pb[qb][r >> 3][r & 7] = two[0];
-    pb[qb][r >> 3][(r & 7) + 1] = two[1];
+    pb[r >> 3][r & 7] = two[0];
+    pb[r >> 3][(r & 7) + 1] = two[1];
   };
-  // element pairs in the order P V consumes them: 16-key chunk, block, element
-  constexpr int NPAIR = 8 * QB;
-  auto pair_qb = [](int i) { return (i >> 2) % QB; };
-  auto pair_r = [](int i) { return 8 * (i / (4 * QB)) + 2 * (i & 3); };
+  // the eight element pairs in the order P V consumes them: 16-key chunk, element
+  constexpr int NPAIR = 8;
+  auto pair_r = [](int i) { return 8 * (i / 4) + 2 * (i & 3); };
   // V^T fragment (A operand of O^T) for 16-key chunk kc and head-dim block db
   // of 32-key half h of the tile in the slot at v_slot
   auto load_v = [&](int v_slot, int h, int kc, int db) __attribute__((always_inline)) {
@@ -340,106 +284,72 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   // (Checking each 16-key half just before its P V products, so that part of
   // the probabilities could still be computed under the P V MFMAs, keeps the
   // sub-tile's scores live across more code and spills at d = 128.)
-  auto step_body = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
-                       __attribute__((always_inline)) {
+  auto step_body = [&](f32x16& cur, f32x16& nxt, int t, int v_slot, int kp_slot) __attribute__((always_inline)) {
     const int h = t & 1;
     const int kp_slot_cur = h ? kp_slot : v_slot;  // slot of sub-tile t + 1 (rest of its K fragments)
-    bf16x8 vf[2][T::NDB], pb[QB][2];
-    float ps0[QB], ps1[QB], mc[QB], alpha[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      ps0[qb] = -0.f;  // x + (-0) = x exactly, so the first add folds away
-      ps1[qb] = -0.f;
-      mc[qb] = m[qb] * c2;
-    }
-    constexpr int EARLY = NPAIR;  // every pair is computed under the score MFMAs
-    // The score MFMAs run at raised wave priority: when both waves of a SIMD
-    // can issue, the one feeding the matrix core goes first (measured 1-2%).
+    bf16x8 vf[2][T::NDB], pb[2];
+    float ps0 = -0.f, ps1 = -0.f;  // x + (-0) = x exactly, so the first add folds away
+    float mc = m * c2;
+    // Every probability pair is computed under the score MFMAs, which run at
+    // raised wave priority: when both waves of a SIMD can issue, the one
+    // feeding the matrix core goes first (measured 1-2%).
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int c = 0; c < T::NC; ++c) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) nxt[qb] = mfma32x32x16(kf[c], qop[qb][c], c == 0 ? (f32x16){} : nxt[qb]);
+      nxt = mfma32x32x16(kf[c], qop[c], c == 0 ? (f32x16){} : nxt);
       if (c + 2 < T::NC) kf[c + 2] = k_frag(kp_slot_cur, (t + 1) & 1, c + 2);
 #pragma unroll
-      for (int i = EARLY * c / T::NC; i < EARLY * (c + 1) / T::NC; ++i)
-        prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
+      for (int i = NPAIR * c / T::NC; i < NPAIR * (c + 1) / T::NC; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_r(i));
       if (c < T::NDB) vf[0][c] = load_v(v_slot, h, 0, c);  // the 16-key chunk kc = 1 follows below
     }
     __builtin_amdgcn_s_setprio(0);
-    {
-      float chk[QB];
+    if (over_limit(ps0 + ps1)) {
+      raise_ref(cur);
+      ps0 = -0.f;
+      ps1 = -0.f;
+      mc = m * c2;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) chk[qb] = ps0[qb] + ps1[qb];
-      if (over_limit(chk)) {
-        raise_ref(cur, alpha);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          ps0[qb] = -0.f;
-          ps1[qb] = -0.f;
-          mc[qb] = m[qb] * c2;
-        }
-#pragma unroll
-        for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
-      }
+      for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_r(i));
     }
 #pragma unroll
     for (int i = 0; i < 2 * T::NDB; ++i) {
       const int kc = i / T::NDB, db = i % T::NDB;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], vf[kc][db], pb[qb][kc]);
+      oacc[db] = mfma32x32x16(vf[kc][db], pb[kc], oacc[db]);
       if (i < T::NDB) vf[1][i] = load_v(v_slot, h, 1, i);
       if (i >= 2 * T::NDB - 2) kf[i - (2 * T::NDB - 2)] = k_frag(kp_slot, h, i - (2 * T::NDB - 2));
     }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps0[qb] + ps1[qb];
+    lsum += ps0 + ps1;
   };
   // the same when sub-tile t + 1 is known to be fully visible
-  auto clean_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
-                        __attribute__((always_inline)) { step_body(cur, nxt, t, v_slot, kp_slot); };
-  auto full_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
-                       __attribute__((always_inline)) {
+  auto clean_step = [&](f32x16& cur, f32x16& nxt, int t, int v_slot, int kp_slot) __attribute__((always_inline)) {
+    step_body(cur, nxt, t, v_slot, kp_slot);
+  };
+  auto full_step = [&](f32x16& cur, f32x16& nxt, int t, int v_slot, int kp_slot) __attribute__((always_inline)) {
     step_body(cur, nxt, t, v_slot, kp_slot);
     if (needs_mask(t + 1)) mask(nxt, t + 1);
   };
   // the wave's last sub-tile: probabilities and P V only
-  auto last_step = [&](f32x16(&cur)[QB], int t, int v_slot) __attribute__((always_inline)) {
-    bf16x8 pb[QB][2];
-    float ps0[QB], ps1[QB], mc[QB], alpha[QB], chk[QB];
+  auto last_step = [&](f32x16& cur, int t, int v_slot) __attribute__((always_inline)) {
+    bf16x8 pb[2];
+    float ps0 = -0.f, ps1 = -0.f;
+    float mc = m * c2;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      ps0[qb] = -0.f;
-      ps1[qb] = -0.f;
-      mc[qb] = m[qb] * c2;
-    }
+    for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_r(i));
+    if (over_limit(ps0 + ps1)) {
+      raise_ref(cur);
+      ps0 = -0.f;
+      ps1 = -0.f;
+      mc = m * c2;
 #pragma unroll
-    for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) chk[qb] = ps0[qb] + ps1[qb];
-    if (over_limit(chk)) {
-      raise_ref(cur, alpha);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        ps0[qb] = -0.f;
-        ps1[qb] = -0.f;
-        mc[qb] = m[qb] * c2;
-      }
-#pragma unroll
-      for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_qb(i), pair_r(i));
+      for (int i = 0; i < NPAIR; ++i) prob_pair(cur, pb, ps0, ps1, mc, pair_r(i));
     }
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db) {
-        const bf16x8 a = load_v(v_slot, t & 1, kc, db);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) pv_mfma<QB>(oacc[qb][db], a, pb[qb][kc]);
-      }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) lsum[qb] += ps0[qb] + ps1[qb];
+      for (int db = 0; db < T::NDB; ++db) oacc[db] = mfma32x32x16(load_v(v_slot, t & 1, kc, db), pb[kc], oacc[db]);
+    lsum += ps0 + ps1;
   };
-  auto tail_step = [&](f32x16(&cur)[QB], f32x16(&nxt)[QB], int t, int v_slot, int kp_slot)
-                       __attribute__((always_inline)) {
+  auto tail_step = [&](f32x16& cur, f32x16& nxt, int t, int v_slot, int kp_slot) __attribute__((always_inline)) {
     if (t + 1 < n_st)
       full_step(cur, nxt, t, v_slot, kp_slot);
     else if (t < n_st)
@@ -464,10 +374,9 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   if (n_kt > 3) dma(3, 3);
   if (n_st > 0) {
     // sub-tile 0 sets the first reference (from m = -inf: alpha = 0)
-    float alpha0[QB];
     qk(sA, 0, 0);
     if (needs_mask(0)) mask(sA, 0);
-    raise_ref(sA, alpha0);
+    raise_ref(sA);
   }
   kf[0] = k_frag(0, 1, 0);  // sub-tile 1 (tile 0, second half)
   kf[1] = k_frag(0, 1, 1);
@@ -507,61 +416,59 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void fwd_bf16_kernel(const uint16
   }
 
   // ---- epilogue: O = acc / l, one rounding to bf16; LSE in natural log ----
-  o_fence(oacc);
+  const float ltot = halves_sum(lsum);
+  if (qrow < N) {
+    const float inv = 1.f / ltot;
+    uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = halves_sum(lsum[qb]);
-    const int qrow = wq0 + 32 * qb + lq;
-    if (qrow < N) {
-      const float inv = 1.f / ltot;
-      uint16_t* orow = O + head + (size_t)qrow * D;
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < T::NDB; ++db)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const bf16x2 a = to_bf16x2(oacc[qb][db][4 * rb] * inv, oacc[qb][db][4 * rb + 1] * inv);
-          const bf16x2 b = to_bf16x2(oacc[qb][db][4 * rb + 2] * inv, oacc[qb][db][4 * rb + 3] * inv);
-          const bf16x4 four = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-          *(bf16x4*)(orow + 32 * db + 8 * rb + 4 * hf) = four;
-        }
-      if (LSE != nullptr && hf == 0) LSE[(size_t)bh * N + qrow] = m[qb] * scale + __logf(ltot);
-    }
+      for (int rb = 0; rb < 4; ++rb) {
+        const bf16x2 a = to_bf16x2(oacc[db][4 * rb] * inv, oacc[db][4 * rb + 1] * inv);
+        const bf16x2 b = to_bf16x2(oacc[db][4 * rb + 2] * inv, oacc[db][4 * rb + 3] * inv);
+        const bf16x4 four = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+        *(bf16x4*)(orow + 32 * db + 8 * rb + 4 * hf) = four;
+      }
+    if (LSE != nullptr && hf == 0) LSE[(size_t)bh * N + qrow] = m * scale + __logf(ltot);
   }
 }
 
-#ifndef FA_FWD_QB
-#define FA_FWD_QB 1
-#endif
-// query blocks of 32 rows per wave: 1 = eight waves (two per SIMD, the
-// hardware interleaves them), 2 = four waves with every LDS fragment feeding
-// two MFMAs (with every probability computed under the score MFMAs, that
-// variant keeps both blocks' probabilities live and spills at d = 128)
-constexpr int kFwdQB = FA_FWD_QB;
+// A launch with fewer workgroups than this per CU takes 128-row tiles at
+// d = 64 (two 4-wave workgroups per CU instead of one 8-wave one): the grid
+// doubles and the heaviest causal tile, which sets the time of a short
+// launch, halves.
+constexpr int kSmallGridPerCU = 2;
+constexpr int kNumCU = 256;
 
-template <int D, bool CAUSAL>
+template <int D, int NW, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                     int N, float scale, hipStream_t s) {
-  using T = FwdTile<D, kFwdQB>;
+  using T = FwdTile<D, NW>;
   const int n_qt = (N + T::BR - 1) / T::BR;
   const int BH = B * H;
   // exp2 units; a positive floor keeps masked (-inf) scores at probability 0
   // when scale is 0 (every visible probability is then exp2(~0) = 1)
   float c2 = scale * kLog2e;
   if (!(c2 >= FLT_MIN)) c2 = FLT_MIN;
-  dim3 grid((unsigned)(n_qt * BH)), block(64 * T::NW);
+  dim3 grid((unsigned)(n_qt * BH)), block(64 * NW);
   const uint16_t *qp = (const uint16_t*)q, *kp = (const uint16_t*)k, *vp = (const uint16_t*)v;
   uint16_t* op = (uint16_t*)o;
   void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &scale, &c2, (void*)&n_qt, (void*)&BH};
-  return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, kFwdQB, CAUSAL>, grid, block, args, 0, s);
+  return hipLaunchKernel((const void*)&fwd_bf16_kernel<D, NW, CAUSAL>, grid, block, args, 0, s);
 }
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
                            int d, bool causal, float scale, hipStream_t s) {
-  if (d == 64)
-    return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, B, H, N, scale, s)
-                  : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, B, H, N, scale, s);
-  return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, B, H, N, scale, s)
-                : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, B, H, N, scale, s);
+  if (d == 64) {
+    const long long big_tiles = (long long)B * H * ((N + 255) / 256);
+    if (big_tiles < (long long)kSmallGridPerCU * kNumCU)
+      return causal ? launch_fwd_bf16_t<64, 4, true>(q, k, v, o, lse, B, H, N, scale, s)
+                    : launch_fwd_bf16_t<64, 4, false>(q, k, v, o, lse, B, H, N, scale, s);
+    return causal ? launch_fwd_bf16_t<64, 8, true>(q, k, v, o, lse, B, H, N, scale, s)
+                  : launch_fwd_bf16_t<64, 8, false>(q, k, v, o, lse, B, H, N, scale, s);
+  }
+  return causal ? launch_fwd_bf16_t<128, 8, true>(q, k, v, o, lse, B, H, N, scale, s)
+                : launch_fwd_bf16_t<128, 8, false>(q, k, v, o, lse, B, H, N, scale, s);
 }
 
 }  // namespace fa

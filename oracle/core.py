@@ -18,12 +18,15 @@ What it computes, and where that is defined:
   softmax section. It also returns the per-row log-sum-exp
   LSE_i = ln sum_j exp(S_ij), which the pages do not define (reading: natural
   log over the visible keys, in float).
-* ``online_attention`` follows the streaming recurrence of the mantramindai.in
-  page, section "The two ideas", idea 2 and its numpy listing: keep a running
-  max m, running sum l and running output per query row; for each key block,
-  raise m to the block max, shrink the old l and output by exp(m_old - m_new),
-  add the block, and divide by l once at the end. It is an oracle of the
-  algorithm the fused kernel runs, pinned against ``attention``.
+* ``online_attention`` is the streaming recurrence of the mantramindai.in
+  page, section "The two ideas", idea 2: every query row keeps a running max,
+  running sum and running output; each key block's own (max, sum, output) is
+  merged into them, the old sum and output shrinking by exp(m_old - m_new)
+  when the max rises, and the output is divided by the sum once at the end.
+  Written here as a fold of per-block partials with the same merge rule that
+  ``split_decode`` applies to its chunks, vectorised over rows. It is an
+  oracle of the algorithm the fused kernel runs, pinned against
+  ``attention``.
 * ``split_decode`` follows the same page's follow-up on decode (Flash-Decoding):
   one query row, the keys cut into chunks that are processed independently,
   each chunk yielding (max, sum, unnormalised output), and the chunks merged
@@ -107,44 +110,56 @@ def attention(q, k, v, causal: bool, scale: float, rows=None, heads=None):
     return O, L
 
 
-def attention_probs(q, k, causal: bool, scale: float):
-    """The materialised probability matrix P for one head (q, k: [N,d])."""
-    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
-    return _head_attention(q, k, np.zeros((k.shape[0], 1)), causal, _f32(scale))[2]
+def _block_partial(S: np.ndarray, v: np.ndarray):
+    """(max, sum, unnormalised output) of one key block for every row.
+
+    S: [rows, keys] scaled scores of the block (-inf where masked); v: [keys, dv].
+    m = row max of S; l = sum exp(S - m); o = exp(S - m) V. A row with no
+    visible key in the block gives (-inf, 0, 0).
+    """
+    m = S.max(axis=1)
+    finite = np.isfinite(m)
+    P = np.exp(S - np.where(finite, m, 0.0)[:, None])      # exp(-inf) = 0 for masked keys
+    return m, P.sum(axis=1), P @ v
+
+
+def _merge(a, b):
+    """Merge two (max, sum, unnormalised output) triples over disjoint key sets.
+
+    Both are brought to the larger maximum M: sums and outputs are multiplied
+    by exp(m - M) before they are added. A side with m = -inf (no keys)
+    contributes nothing.
+    """
+    (m1, l1, o1), (m2, l2, o2) = a, b
+    M = np.maximum(m1, m2)
+    w1 = np.where(np.isfinite(m1), np.exp(m1 - np.where(np.isfinite(M), M, 0.0)), 0.0)
+    w2 = np.where(np.isfinite(m2), np.exp(m2 - np.where(np.isfinite(M), M, 0.0)), 0.0)
+    return M, w1 * l1 + w2 * l2, w1[:, None] * o1 + w2[:, None] * o2
 
 
 def online_attention(q, k, v, causal: bool, scale: float, block: int):
     """The streaming (online-softmax) recurrence over key blocks, float64, one head.
 
-    q: [N,d], k/v: [Nk,d]. Returns (O, LSE). For every query row: running
-    max m (starts at -inf), running sum l (0) and running output acc (0);
-    per key block: m_new = max(m, block max); shrink l and acc by
-    exp(m - m_new); add exp(scores - m_new) to l and its V-weighted sum to
-    acc; at the end O = acc / l and LSE = m + ln l.
+    q: [N,d], k/v: [Nk,d]. Returns (O, LSE). Every query row carries a
+    running state (max m, sum l, unnormalised output acc), starting empty
+    (-inf, 0, 0). The keys are visited in blocks of ``block``; each block's own
+    (max, sum, output) is merged into the state, which rescales the old sum and
+    output by exp(m_old - m_new) when the maximum rises. At the end O = acc / l
+    and LSE = m + ln l.
     """
     q, k, v = (np.asarray(t, dtype=np.float64) for t in (q, k, v))
     s = _f32(scale)
     N, Nk = q.shape[0], k.shape[0]
-    O = np.zeros((N, v.shape[1]))
-    L = np.zeros(N)
-    for i in range(N):
-        m, l, acc = -np.inf, 0.0, np.zeros(v.shape[1])
-        for start in range(0, Nk, block):
-            stop = min(Nk, start + block)
-            if causal:
-                stop = min(stop, i + 1)                   # keys beyond i are masked
-            if stop <= start:
-                break
-            sb = s * (k[start:stop] @ q[i])
-            m_new = max(m, sb.max())
-            shrink = np.exp(m - m_new)                     # exp(-inf) = 0 on the first block
-            pb = np.exp(sb - m_new)
-            l = l * shrink + pb.sum()
-            acc = acc * shrink + pb @ v[start:stop]
-            m = m_new
-        O[i] = acc / l
-        L[i] = m + np.log(l)
-    return O, L
+    rows = np.arange(N)
+    state = (np.full(N, -np.inf), np.zeros(N), np.zeros((N, v.shape[1])))
+    for start in range(0, Nk, block):
+        keys = np.arange(start, min(Nk, start + block))
+        S = s * (q @ k[keys].T)
+        if causal:
+            S = np.where(keys[None, :] > rows[:, None], -np.inf, S)   # keys beyond the row are masked
+        state = _merge(state, _block_partial(S, v[keys]))
+    m, l, acc = state
+    return acc / l[:, None], m + np.log(l)
 
 
 def decode(q, kc, vc, scale: float | None = None):
@@ -273,13 +288,6 @@ def attention_grad(q, k, v, do, causal: bool, scale: float, heads=None):
     for b, h in pairs:
         dQ[b, h], dK[b, h], dV[b, h] = _head_attention_grad(q[b, h], k[b, h], v[b, h], do[b, h], causal, s)
     return dQ, dK, dV
-
-
-def attention_bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> int:
-    """Backward FLOPs of the recompute method: 10*d per visible (query, key) pair
-    (S recomputed, then dP, dV, dQ and dK, each 2*d)."""
-    pairs = N * (N + 1) // 2 if causal else N * N
-    return 10 * d * B * H * pairs
 
 
 def naive_workspace_bytes(B: int, H: int, N: int, elem_bytes: int) -> int:

@@ -187,6 +187,13 @@ def test_status_strings(lib):
     assert lib.fa_last_hip_error() == 0
 
 
+def test_fwd_f32_rejects_a_grid_past_int(lib):
+    """B*H*ceil(N/64) fits an int, but the fp32 kernel's one workgroup per four rows would need 2^31
+    workgroups: rejected before any launch (fake tensors 2^42 bytes apart, so nothing overlaps)."""
+    g = 1 << 42
+    assert fwd(lib, q=g, k=2 * g, v=3 * g, o=4 * g, lse=5 * g, B=1, H=1 << 12, N=1 << 21, d=64, f32=True) == INVALID
+
+
 def test_binding_errors_are_raised(lib):
     with pytest.raises(binding.FaError) as ei:
         binding._check("fa_fwd", UNSUPPORTED)

@@ -128,7 +128,7 @@ def test_grad_pins(pin):
     assert pin(_oracle_grad)
 
 
-def test_batched_matches_head_and_flops():
+def test_batched_matches_head():
     q, k, v, g = (rnd(70 + i, 2, 3, 10, 4) for i in range(4))
     dq, dk, dv = oracle.attention_grad(q, k, v, g, True, 0.3)
     for b in range(2):
@@ -136,8 +136,6 @@ def test_batched_matches_head_and_flops():
             ref = oa._head_attention_grad(q[b, h], k[b, h], v[b, h], g[b, h], True, float(np.float32(0.3)))
             for x, y in zip((dq[b, h], dk[b, h], dv[b, h]), ref):
                 assert np.array_equal(x, y)
-    assert oracle.attention_bwd_flops(1, 1, 4, 8, True) == 10 * 8 * 10
-    assert oracle.attention_bwd_flops(2, 3, 4, 8, False) == 10 * 8 * 16 * 6
 
 
 # ---- mutation tests: plausible mistakes in copies of the gradient ----
