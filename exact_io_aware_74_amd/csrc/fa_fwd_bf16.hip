@@ -41,7 +41,10 @@
 //    per-sub-tile row maximum is computed, and the rare update sits on a
 //    wave-uniform branch, as does the causal / ragged-tail mask;
 //  * causal: key tiles past the workgroup's last query are never loaded and
-//    sub-tiles past a wave's last query are skipped by that wave;
+//    sub-tiles past a wave's last query are skipped by that wave. The two
+//    waves of a SIMD hold one low and one high row block, so the diagonal's
+//    growing work is the same on every SIMD, and the last three tiles (all
+//    copies in, no slot rewritten) run without barriers;
 //  * heaviest causal query tiles are dispatched first, and consecutive
 //    workgroups take consecutive heads so a head's K/V stays in one XCD's L2.
 #include <float.h>
@@ -105,7 +108,12 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const uint16_
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
-  const int wq0 = q0 + T::WR * w;  // first query row of this wave
+  // Waves w and w + NW/2 share a SIMD. Row block w goes to wave w in the
+  // first half and to wave NW/2 + (NW - 1 - w) in the second, so each SIMD
+  // holds one low and one high row block: in the causal diagonal, where a row
+  // block's work grows with its index, every SIMD then carries the same load.
+  const int rb = w < NW / 2 ? w : (3 * NW / 2 - 1 - w);
+  const int wq0 = q0 + T::WR * rb;  // first query row of this wave
   const int qrow = wq0 + lq;       // the query row this lane's scores and output belong to
 
   // ---- DMA of one K/V tile into a ring slot: instruction v of the tile
@@ -359,13 +367,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const uint16_
   // the next step on) and every wave done with tile j, whose ring slot then
   // receives tile j + 4. A wave's copies complete in issue order, so with
   // tile j + 3 also in flight it waits until only that tile's copies remain.
+  // After the last copy has been issued, one wait for all copies and one
+  // barrier end the synchronisation.
   auto end_tile = [&](int j, int slot) __attribute__((always_inline)) {
-    if (j + 3 < n_kt)
-      wait_vmcnt<2 * T::IPW>();
-    else
+    if (j + 4 < n_kt) {
+      wait_vmcnt<2 * T::IPW>();  // tile j + 3 may still be in flight
+      __syncthreads();
+      dma(j + 4, slot);
+    } else if (j == max(0, n_kt - 4)) {
+      // every tile has been issued: once all copies are in, no slot is
+      // written again, so the last tiles need no barrier and each wave
+      // finishes them at its own pace
       wait_vmcnt<0>();
-    __syncthreads();
-    if (j + 4 < n_kt) dma(j + 4, slot);
+      __syncthreads();
+    }
   };
 
   wait_vmcnt<0>();  // Q, tiles 0 and 1
