@@ -409,7 +409,7 @@ def _short_kernel(name: str) -> str:
         depth += ch == "<"
         depth -= ch == ">"
         out.append(ch)
-    return "".join(out).replace("fa::", "")
+    return "".join(out).replace("fa::", "").replace("anon::", "")
 
 
 def _read_counter_csvs(path):
@@ -482,6 +482,58 @@ def summarize_counters(root: str, write_traffic: bool) -> str:
     return "\n".join(lines)
 
 
+def summarize_pmc(root: str) -> str:
+    """Markdown table of the counter runs under root (each pass its own run, any depth): per kernel and
+    grid, the dispatch time and every collected counter averaged over dispatches, with derived columns
+    where their counters were taken: clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / clock cycles; VALU per MFMA = (SQ_INSTS_VALU -
+    SQ_INSTS_MFMA) / SQ_INSTS_MFMA; HBM bytes = FETCH_SIZE and WRITE_SIZE KiB x 1024, each scaled by
+    the 1 GiB copy of its run (bench.py --copy-calibration)."""
+    import csv
+    import glob
+    per, times = {}, {}
+    for f in sorted(glob.glob(os.path.join(root, "**", "*_counter_collection.csv"), recursive=True)):
+        disp = {}
+        for r in csv.DictReader(open(f)):
+            ent = disp.setdefault(int(r["Dispatch_Id"]), [_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]), {},
+                                                          int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+            ent[2][r["Counter_Name"]] = ent[2].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        scale = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            copies = [v[2][c] for v in disp.values() if "copyBuffer" in v[0] and c in v[2]]
+            if copies:
+                scale[c] = 1048576.0 / max(copies)
+        for k, g, cs, dt in disp.values():
+            if not k.startswith(("fwd_", "bwd_", "decode_", "naive_")):
+                continue
+            for c, v in cs.items():
+                if c in ("FETCH_SIZE", "WRITE_SIZE"):
+                    if c not in scale:
+                        continue
+                    v = v * 1024 * scale[c]
+                per.setdefault((k, g), {}).setdefault(c, []).append(v)
+            times.setdefault((k, g), []).append(dt)
+    avg = lambda xs: sum(xs) / len(xs)
+    lines = ["| kernel | grid (threads) | dispatch us | clock GHz | MFMA busy | MFMA instr (M) | VALU per MFMA "
+             "| LDS instr (M) | LDS bank-conflict cycles (M) | HBM read bytes | HBM write bytes |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (k, g), cs in sorted(per.items(), key=lambda kv: -avg(times[kv[0]])):
+        c = {n: avg(v) for n, v in cs.items()}
+        t = avg(times[(k, g)])
+        cyc = c.get("GRBM_GUI_ACTIVE", 0) / 8
+        f = lambda x, fmt: (fmt.format(x) if x is not None else "-")
+        clock = cyc / t if cyc else None
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / cyc if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in c else None
+        mfma = c.get("SQ_INSTS_MFMA")
+        vpm = (c["SQ_INSTS_VALU"] - mfma) / mfma if mfma and "SQ_INSTS_VALU" in c else None
+        lines.append(f"| `{k}` | {g} | {t / 1e3:.1f} | {f(clock, '{:.2f}')} | {f(busy, '{:.0%}')} | "
+                     f"{f(mfma / 1e6 if mfma else None, '{:.2f}')} | {f(vpm, '{:.1f}')} | "
+                     f"{f(c['SQ_INSTS_LDS'] / 1e6 if 'SQ_INSTS_LDS' in c else None, '{:.1f}')} | "
+                     f"{f(c['SQ_LDS_BANK_CONFLICT'] / 1e6 if 'SQ_LDS_BANK_CONFLICT' in c else None, '{:.2f}')} | "
+                     f"{f(c.get('FETCH_SIZE'), '{:.4g}')} | {f(c.get('WRITE_SIZE'), '{:.4g}')} |")
+    return "\n".join(lines)
+
+
 def summarize_stats(csv_path: str) -> str:
     """Markdown table (kernel, grid, dispatches, avg/min/max us) from a rocprofv3 kernel trace CSV."""
     import csv
@@ -532,12 +584,18 @@ def main():
                          "profiles/traffic_fwd_bf16_n8192.json (with the current kernel source digest)")
     ap.add_argument("--summarize-stats", metavar="CSV", default=None,
                     help="no GPU: print the markdown table of a rocprofv3 kernel trace CSV")
+    ap.add_argument("--summarize-pmc", metavar="DIR", default=None,
+                    help="no GPU: print the markdown table of every counter run under DIR (kernel, grid, "
+                         "derived clock, MFMA busy, VALU per MFMA, LDS, calibrated HBM bytes)")
     args = ap.parse_args()
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters, args.write_traffic_record))
         return
     if args.summarize_stats:
         print(summarize_stats(args.summarize_stats))
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this library has no multi-GPU path (asked for --gpus {args.gpus})",
