@@ -30,18 +30,26 @@ def check_cover(cover, N, causal):
     np.testing.assert_array_equal(cover, visible(N, causal).astype(np.int64))
 
 
-def fwd_bf16_model(N, causal):
-    """fwd_bf16_kernel, one query block of 32 rows per wave: 256-row workgroups, 64-key tiles,
-    32-key sub-tiles; sub-tiles 1 .. 2*j_clean are scored in the unmasked loop."""
-    BR, BC = 256, 64
+def fwd_bf16_model(N, causal, NW=8):
+    """fwd_bf16_kernel with NW waves of 32 query rows per workgroup (8: 256-row workgroups; 4: the
+    128-row ones taken at d = 64 for small grids), 64-key tiles, 32-key sub-tiles; row block b sits
+    on wave b for b < NW/2 and on wave 3NW/2 - 1 - b otherwise; sub-tiles 1 .. 2*j_clean are scored
+    in the unmasked loop. Also checks the copy ring: every tile a wave reads during tile iteration j
+    (tiles j and j + 1) was published by a barrier before that iteration, and a slot is rewritten
+    only after a barrier that follows every read of its previous tile."""
+    BR, BC = 32 * NW, 64
     cover = np.zeros((N, N), dtype=np.int64)
     scored = 0
     for qt in range(math.ceil(N / BR)):
         q0 = qt * BR
         kv_end = min(N, q0 + BR) if causal else N
         n_kt = math.ceil(kv_end / BC)
-        for w in range(8):
-            wq0 = q0 + 32 * w
+        ring_protocol(n_kt)
+        blocks = sorted(w if w < NW // 2 else 3 * NW // 2 - 1 - w for w in range(NW))
+        assert blocks == list(range(NW))          # the wave -> row block map is a permutation
+        for w in range(NW):
+            rb = w if w < NW // 2 else 3 * NW // 2 - 1 - w
+            wq0 = q0 + 32 * rb
             wv_end = min(N, wq0 + 32) if causal else N
             n_st = math.ceil(wv_end / 32) if wq0 < N else 0
             assert n_st <= 2 * n_kt
@@ -59,6 +67,39 @@ def fwd_bf16_model(N, causal):
                 cover[r0:r1, k0:min(k1, N)] += vis
                 scored += (r1 - r0) * 32
     return cover, scored
+
+
+def ring_protocol(n_kt, nbuf=4):
+    """The forward's copy ring for one workgroup: tiles 0 and 1 copied and published before the loop,
+    tiles 2 and 3 copied right after; end of tile j: if j + 4 < n_kt, wait until tile j + 2 is in,
+    barrier, copy tile j + 4 into tile j's slot; at j = max(0, n_kt - 4), wait for every copy and
+    barrier; later tiles have no barrier."""
+    issued = {}                                    # tile -> slot
+    published = set()
+    slot_holds = {}                                # slot -> tile
+    def issue(t):
+        s = t % nbuf
+        if s in slot_holds:
+            assert slot_holds[s] in done_reading, (n_kt, t)   # previous tile of the slot fully read
+        slot_holds[s] = t
+        issued[t] = s
+    done_reading = set()
+    for t in range(min(2, n_kt)):
+        issue(t)
+    published |= set(issued)
+    for t in range(2, min(4, n_kt)):
+        issue(t)
+    for j in range(n_kt):
+        for t in (j, j + 1):                       # tiles read during iteration j
+            if t < n_kt:
+                assert t in published, (n_kt, j, t)
+        done_reading.add(j)                        # nothing reads tile j after iteration j
+        if j + 4 < n_kt:
+            published |= {t for t in issued if t <= j + 2}
+            issue(j + 4)
+        elif j == max(0, n_kt - 4):
+            published |= set(issued)
+    assert set(issued) == set(range(n_kt))
 
 
 def fwd_fp8_model(N, causal):
@@ -144,11 +185,39 @@ def bwd_dq_model(N, causal):
     return cover
 
 
+@pytest.mark.parametrize("NW", [8, 4])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SIZES)
-def test_forward_bf16_tiles(N, causal):
-    cover, _ = fwd_bf16_model(N, causal)
+def test_forward_bf16_tiles(N, causal, NW):
+    cover, _ = fwd_bf16_model(N, causal, NW)
     check_cover(cover, N, causal)
+
+
+@pytest.mark.parametrize("n_kt", list(range(1, 40)))
+def test_forward_copy_ring(n_kt):
+    ring_protocol(n_kt)
+
+
+def test_forward_copy_ring_catches_an_early_rewrite():
+    """A ring whose last barrier comes one tile too early (the barrier-free stretch one tile longer)
+    reads a tile no barrier published: the model rejects it."""
+    def too_early(n_kt, nbuf=4):
+        published, issued = set(), set()
+        for t in range(min(4, n_kt)):
+            issued.add(t)
+        published |= {0, 1} & issued
+        for j in range(n_kt):
+            for t in (j, j + 1):
+                if t < n_kt and t not in published:
+                    return False
+            if j + 5 < n_kt:
+                published |= {t for t in issued if t <= j + 2}
+                issued.add(j + 4)
+            elif j == max(0, n_kt - 5):
+                issued |= set(range(n_kt))
+                published |= {t for t in issued if t <= j + 2}
+        return True
+    assert not all(too_early(n) for n in range(1, 40))
 
 
 def test_forward_bf16_masked_work_is_small():
