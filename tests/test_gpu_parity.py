@@ -305,3 +305,13 @@ def test_joint_key_value_permutation_and_query_permutation(d):
     assert_lse_close(to_f64(l1), Lref, "bf16")
     assert_close(to_f64(o2), Oref[:, :, pq], "bf16", what="O with Q rows permuted")
     assert_lse_close(to_f64(l2), Lref[:, :, pq], "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_d64_large_grid_takes_the_eight_wave_path(causal):
+    """At d = 64 the launcher takes 128-row workgroups only when 256-row tiles would give fewer than two
+    workgroups per CU (512 tiles); B=1 H=32 N=4096 has exactly 512, so this runs the 256-row, eight-wave
+    kernel (N ragged by one key past a tile in the second case). Every element against the oracle."""
+    N = 4096 if causal else 4095
+    q, k, v = si.random_case(9300 + N, 1, 32, N, 64, "bf16", std=1.5)
+    print("d64 eight-wave", causal, _fwd_case(q, k, v, "bf16", causal, fa.default_scale(64)))
