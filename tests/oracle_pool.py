@@ -14,6 +14,8 @@ import multiprocessing as mp
 import os
 from concurrent.futures import ProcessPoolExecutor, as_completed
 
+import numpy as np
+
 import oracle
 import seeded_inputs as si
 
@@ -32,6 +34,14 @@ def forward_head(name: str, b: int, h: int):
     q, k, v = (si.as_float64(si.tensor_slice(w, t, b, h), w.dtype)[None, None] for t in ("q", "k", "v"))
     O, L = oracle.attention(q, k, v, w.causal, w.scale)
     return b, h, O[0, 0], L[0, 0]
+
+
+def fp8_forward_head(key, q8, k8, v8, descales, causal: bool, scale: float):
+    """Oracle O and LSE of one head of FP8 inputs: the plain definition on the dequantised values
+    (descale x e4m3 value, exact in float64). q8, k8, v8: that head's [N, d] e4m3 codes."""
+    q, k, v = (si.fp8_as_float64(x, ds)[None, None] for x, ds in zip((q8, k8, v8), descales))
+    O, L = oracle.attention(q, k, v, causal, scale)
+    return key, O[0, 0], L[0, 0], float(np.abs(v).max())
 
 
 def decode_heads(name: str, b: int, hs):
