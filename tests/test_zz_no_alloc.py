@@ -68,3 +68,31 @@ def test_noalloc_rejects_a_problem_past_the_array():
     assert ei.value.status == -5
     torch.cuda.synchronize()
     assert (o == 3.0).all().item()
+
+
+def test_noalloc_replays_from_a_captured_graph():
+    """The use it exists for: captured in a HIP graph (no allocation, no synchronisation inside), each replay
+    recomputes from the current inputs and equals an eager fa_decode bit for bit. The inputs are rewritten
+    between replays, with eager work and host synchronisations in between."""
+    (q, k, v), _ = _case(103, 2, 4, 1500, 128)
+    (q2, k2, v2), _ = _case(104, 2, 4, 1500, 128)
+    srcs = [(q.clone(), k.clone(), v.clone()), (q2, k2, v2)]
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # first call outside capture (address lookup)
+        fa.decode(q, k, v, nsplit=32, out=out, noalloc=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.decode(q, k, v, nsplit=32, out=out, noalloc=True)
+    for i in (0, 1, 0, 1):
+        for dst, x in zip((q, k, v), srcs[i]):
+            dst.copy_(x)
+        want = fa.decode(q, k, v, nsplit=32)          # eager, allocating path
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want)
