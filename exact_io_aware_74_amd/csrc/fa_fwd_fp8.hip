@@ -29,7 +29,12 @@
 //    running reference maximum is raised when a unit exceeds it by more than
 //    2 in exp2 units, so every probability is at most 2^8 (e4m3 holds 448) and
 //    those down to 2^-12 of the reference stay normal numbers. The row sum
-//    takes the unrounded fp32 probabilities.
+//    takes the unrounded fp32 probabilities;
+//  * software pipeline over 64-key units: the score MFMAs of unit u + 1 run
+//    with unit u's probabilities between them (unit u's V^T reads in flight
+//    meanwhile), then the P V MFMAs of unit u with the K reads of unit u + 2
+//    in flight and unit u + 1's row maximum and reference update after them,
+//    so every unit's reference is settled before its probabilities are taken.
 #include <float.h>
 
 #include "fa_device.h"
@@ -214,33 +219,22 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) oacc[db] = (f32x16){};
 
-  // One unit: P V for unit u from its scores `cur`, while the scores of unit
-  // u + 1 are computed into `nxt` and the K rows of unit u + 2 are read. That
-  // read is unconditional: past the last unit it reads a ring slot (in bounds,
-  // possibly being refilled) into fragments nobody uses, and it keeps the
-  // fragments in one set of registers (a conditional read costs a 32-register
-  // copy per unit).
-  // (the ring offsets of units u and u + 2 come in as vb_u and kb_u2)
-  auto step = [&](f32x16(&cur)[2], f32x16(&nxt)[2], int u, int vb_u, int kb_u2) __attribute__((always_inline)) {
-    if (u >= n_u) return;
-    if (u + 1 < n_u) {
-      qk(nxt, kf);
-      read_k(kf, kb_u2);
-    }
-    if ((64 * u + 64 > N) || (CAUSAL && 64 * u + 63 > wq0)) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 64 * u + 32 * st + (r & 3) + 8 * (r >> 2) + 4 * hf;
-          if (!(key < N && (!CAUSAL || key <= wq0 + lq))) cur[st][r] = -INFINITY;
-        }
-    }
-    float x = cur[0][0];
+  auto needs_mask = [&](int u) __attribute__((always_inline)) {
+    return (64 * u + 64 > N) || (CAUSAL && 64 * u + 63 > wq0);
+  };
+  auto mask_unit = [&](f32x16(&s)[2], int u) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x = fmaxf(x, cur[st][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = 64 * u + 32 * st + (r & 3) + 8 * (r >> 2) + 4 * hf;
+        if (!(key < N && (!CAUSAL || key <= wq0 + lq))) s[st][r] = -INFINITY;
+      }
+  };
+  // The reference update for a unit whose in-lane maximum is x: raised (O and
+  // the running sum rescaled) only when the unit exceeds it by more than the
+  // threshold.
+  auto update_ref = [&](float x) __attribute__((always_inline)) {
     const float mt = halves_max(x);
     if (__builtin_amdgcn_ballot_w64((mt - m) * c2 > kP8Threshold) != 0) {
       const float m_new = fmaxf(m, mt);
@@ -252,28 +246,68 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    const float mc = m * c2 - (float)kP8Shift;
-    float ps = 0.f;
+  };
+  auto unit_max = [&](const f32x16(&s)[2]) __attribute__((always_inline)) {
+    float x0 = fmaxf(s[0][0], s[0][1]), x1 = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      const int st = wd >> 2, r0 = 4 * (wd & 3);
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(fmaf(cur[st][r0 + i], c2, -mc));
-        ps += p[i];
-      }
-      // the conversion writes one half of the word and keeps the other; the
-      // previous word stands in for it (overwritten next), so no zero is set
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[wd], false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-      pb[wd] = word;
+    for (int r = 2; r < 16; ++r) {
+      x0 = fmaxf(x0, s[0][r]);
+      x1 = fmaxf(x1, s[1][r]);
     }
-    lsum += ps;
-    i32x8 vf[T::NDB];
-    read_v(vf, vb_u);
+    return fmaxf(x0, x1);
+  };
+  // Probabilities of word wd (four scores) of a unit, converted to e4m3 into pb.
+  auto probs = [&](const f32x16(&cur)[2], float mc, float& ps, int wd) __attribute__((always_inline)) {
+    const int st = wd >> 2, r0 = 4 * (wd & 3);
+    float p[4];
 #pragma unroll
-    for (int db = 0; db < T::NDB; ++db) oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(cur[st][r0 + i], c2, -mc));
+    ps += (p[0] + p[1]) + (p[2] + p[3]);
+    // the conversion writes one half of the word and keeps the other; the
+    // previous word stands in for it (overwritten next), so no zero is set
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pb[wd], false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+    pb[wd] = word;
+  };
+  // One unit u (u < n_u): `cur` holds its masked scores and the reference
+  // already covers them; kf holds the K rows of unit u + 1. The score MFMAs of
+  // unit u + 1 run with this unit's probabilities between them; then the P V
+  // MFMAs of unit u, then the mask, row maximum and reference update of unit
+  // u + 1. The score MFMAs and the K read of unit u + 2 are unconditional:
+  // past the last unit they read an in-range ring slot into registers nobody
+  // uses (a conditional read costs a 32-register copy per unit). The
+  // scheduling barriers keep the V and K reads where they are issued, ahead
+  // of the arithmetic that hides their latency.
+  auto step = [&](f32x16(&cur)[2], f32x16(&nxt)[2], int u, int vb_u, int kb_u2, bool clean)
+                  __attribute__((always_inline)) {
+    if (u >= n_u) return;
+    const bool has_next = clean || u + 1 < n_u;
+    const float mc = m * c2 - (float)kP8Shift;
+    float ps0 = 0.f, ps1 = 0.f;
+    constexpr int NS = 2 * T::NQ;
+    i32x8 vf[T::NDB];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int st = i & 1, c = i >> 1;
+      nxt[st] = mfma_fp8(kf[st][c], qop[c], c == 0 ? (f32x16){} : nxt[st]);
+      if (i == 0) {
+        read_v(vf, vb_u);  // V reads in flight under the probabilities
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int wd = 8 * i / NS; wd < 8 * (i + 1) / NS; ++wd) probs(cur, mc, wd < 4 ? ps0 : ps1, wd);
+    }
+    lsum += ps0 + ps1;
+    if (!clean && has_next && needs_mask(u + 1)) mask_unit(nxt, u + 1);
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db) {
+      oacc[db] = mfma_fp8(vf[db], pb, oacc[db]);
+      if (db == 0) {
+        read_k(kf, kb_u2);  // K reads of unit u + 2 in flight under the P V MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (has_next) update_ref(unit_max(nxt));
   };
   // End of tile j: tile j + 2 resident for every wave and every wave done with
   // tile j, whose slot then receives tile j + 4.
@@ -293,23 +327,29 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   if (n_u > 0) {
     read_k(kf, unit_base(0));
     qk(sA, kf);
-    if (n_u > 1) read_k(kf, unit_base(1));
+    read_k(kf, unit_base(1));  // unit 1 is in tile 0 (in range even when unused)
+    if (needs_mask(0)) mask_unit(sA, 0);
+    update_ref(unit_max(sA));  // from m = -inf: alpha = 0
   }
-  // Unrolled over the 4-slot ring (j is a multiple of 4 at its top), so every
-  // ring offset is a compile-time constant folded into the LDS instructions.
+  // Leading units whose successor needs no mask: tiles whose two steps both
+  // satisfy that run the straight-line step. Unrolled over the 4-slot ring
+  // (j is a multiple of 4 at its top), so every ring offset is a compile-time
+  // constant folded into the LDS instructions.
   static_assert(T::NBUF == 4, "the unrolled loop walks a 4-slot ring");
+  const int n_clean = min(CAUSAL ? (wq0 + 1) / 64 : N / 64, N / 64);
+  const int j_clean = max(0, (n_clean - 1) / 2);
   int j = 0;
-  for (; j + 4 <= n_kt; j += 4) {
+  for (; j + 4 <= j_clean; j += 4) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      step(sA, sB, 2 * (j + r), unit_base(2 * r), unit_base(2 * r + 2));
-      step(sB, sA, 2 * (j + r) + 1, unit_base(2 * r + 1), unit_base(2 * r + 3));
+      step(sA, sB, 2 * (j + r), unit_base(2 * r), unit_base(2 * r + 2), true);
+      step(sB, sA, 2 * (j + r) + 1, unit_base(2 * r + 1), unit_base(2 * r + 3), true);
       end_tile(j + r, r);
     }
   }
   for (; j < n_kt; ++j) {
-    step(sA, sB, 2 * j, unit_base(2 * j), unit_base(2 * j + 2));
-    step(sB, sA, 2 * j + 1, unit_base(2 * j + 1), unit_base(2 * j + 3));
+    step(sA, sB, 2 * j, unit_base(2 * j), unit_base(2 * j + 2), false);
+    step(sB, sA, 2 * j + 1, unit_base(2 * j + 1), unit_base(2 * j + 3), false);
     end_tile(j, j & 3);
   }
 

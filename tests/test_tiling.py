@@ -104,7 +104,9 @@ def ring_protocol(n_kt, nbuf=4):
 
 def fwd_fp8_model(N, causal):
     """fwd_fp8_kernel: 256-row workgroups, 128-key tiles, 64-key units; a unit is masked only
-    when it holds keys past N or (causal) keys after the wave's first row."""
+    when it holds keys past N or (causal) keys after the wave's first row. Tiles j < j_clean run
+    the straight-line step, which masks nothing and takes a next unit for granted: units
+    1 .. 2*j_clean must need no mask and exist."""
     BR, BC = 256, 128
     cover = np.zeros((N, N), dtype=np.int64)
     for qt in range(math.ceil(N / BR)):
@@ -116,10 +118,15 @@ def fwd_fp8_model(N, causal):
             wv_end = min(N, wq0 + 32) if causal else N
             n_u = math.ceil(wv_end / 64) if wq0 < N else 0
             assert n_u <= 2 * n_kt
+            n_clean = min((wq0 + 1) // 64 if causal else N // 64, N // 64)
+            j_clean = max(0, (n_clean - 1) // 2)
+            assert n_u == 0 or j_clean == 0 or 2 * j_clean < n_u   # waves past N return at once
             r0, r1 = wq0, min(wq0 + 32, N)
             for u in range(n_u):
                 k0, k1 = 64 * u, 64 * u + 64
                 masked = (64 * u + 64 > N) or (causal and 64 * u + 63 > wq0)
+                if 1 <= u <= 2 * j_clean:
+                    assert not masked, (N, qt, w, u)
                 vis = visible(N, causal)[r0:r1, k0:min(k1, N)]
                 if not masked:
                     assert vis.all() and k1 <= N
