@@ -120,7 +120,11 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   const uint8_t* Qh = Q + head;
   const uint8_t* Kh = K + head;
   const uint8_t* Vh = V + head;
-  const int wq0 = q0 + 32 * w;
+  // Waves w and w + 4 share a SIMD. Row block w goes to wave w for w < 4 and
+  // to wave 11 - w otherwise, so each SIMD holds one low and one high row
+  // block and carries the same work in the causal diagonal.
+  const int rb = w < T::NW / 2 ? w : (3 * T::NW / 2 - 1 - w);
+  const int wq0 = q0 + 32 * rb;
 
   // copy instruction v of a tile moves keys KPI*v .. + KPI - 1 (1 KB); lane l
   // fetches the logical chunk that its LDS position holds
@@ -286,6 +290,9 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     float ps0 = 0.f, ps1 = 0.f;
     constexpr int NS = 2 * T::NQ;
     i32x8 vf[T::NDB];
+    // the score MFMA stretch runs at raised wave priority: when both waves of
+    // a SIMD can issue, the one feeding the matrix core goes first
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int st = i & 1, c = i >> 1;
@@ -297,6 +304,7 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
 #pragma unroll
       for (int wd = 8 * i / NS; wd < 8 * (i + 1) / NS; ++wd) probs(cur, mc, wd < 4 ? ps0 : ps1, wd);
     }
+    __builtin_amdgcn_s_setprio(0);
     lsum += ps0 + ps1;
     if (!clean && has_next && needs_mask(u + 1)) mask_unit(nxt, u + 1);
 #pragma unroll
@@ -309,15 +317,22 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
     }
     if (has_next) update_ref(unit_max(nxt));
   };
-  // End of tile j: tile j + 2 resident for every wave and every wave done with
-  // tile j, whose slot then receives tile j + 4.
+  // End of tile j: tile j + 2 resident for every wave (its K rows are read
+  // from the next tile's steps on) and every wave done with tile j, whose
+  // slot then receives tile j + 4. A wave's copies complete in issue order, so
+  // with tile j + 3 also in flight it waits until only that tile's copies
+  // remain. Once the last copy has been issued, one wait for all copies and
+  // one barrier end the synchronisation: no slot is written again, and each
+  // wave finishes the last tiles at its own pace.
   auto end_tile = [&](int j, int slot) __attribute__((always_inline)) {
-    if (j + 3 < n_kt)
+    if (j + 4 < n_kt) {
       wait_vmcnt<2 * T::IPW>();
-    else
+      __syncthreads();
+      dma(j + 4, slot);
+    } else if (j == max(0, n_kt - 4)) {
       wait_vmcnt<0>();
-    __syncthreads();
-    if (j + 4 < n_kt) dma(j + 4, slot);
+      __syncthreads();
+    }
   };
 
   wait_vmcnt<0>();  // Q, tiles 0 and 1

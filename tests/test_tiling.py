@@ -104,7 +104,9 @@ def ring_protocol(n_kt, nbuf=4):
 
 def fwd_fp8_model(N, causal):
     """fwd_fp8_kernel: 256-row workgroups, 128-key tiles, 64-key units; a unit is masked only
-    when it holds keys past N or (causal) keys after the wave's first row. Tiles j < j_clean run
+    when it holds keys past N or (causal) keys after the wave's first row. Row blocks sit on the
+    waves as in the bf16 kernel, and the copy ring follows the same protocol (during tile j a wave
+    reads tiles j and j + 1). Tiles j < j_clean run
     the straight-line step, which masks nothing and takes a next unit for granted: units
     1 .. 2*j_clean must need no mask and exist."""
     BR, BC = 256, 128
@@ -113,8 +115,10 @@ def fwd_fp8_model(N, causal):
         q0 = qt * BR
         kv_end = min(N, q0 + BR) if causal else N
         n_kt = math.ceil(kv_end / BC)
+        ring_protocol(n_kt)
         for w in range(8):
-            wq0 = q0 + 32 * w
+            rb = w if w < 4 else 11 - w
+            wq0 = q0 + 32 * rb
             wv_end = min(N, wq0 + 32) if causal else N
             n_u = math.ceil(wv_end / 64) if wq0 < N else 0
             assert n_u <= 2 * n_kt
