@@ -744,9 +744,10 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
                      "kernel": "fwd_bf16_kernel<128, causal>", "algorithmic_flop_per_launch": flops,
                      "kernel_ms": round(fwd_avg, 4),
-                     "note": "peak is the published 2.4 GHz figure; under this kernel's load the GPU clocks at about "
-                             "1.67-1.76 GHz (GRBM_GUI_ACTIVE counters), where the matrix core is busy about 60% "
-                             "of the cycles"},
+                     "note": "peak is the published 2.4 GHz figure; under this kernel's load the board draws "
+                             "about 1350 W (of its 1400 W) and the XCDs clock at about 1.65-1.88 GHz (amd-smi "
+                             "samples, GRBM_GUI_ACTIVE counters), where the matrix core is busy about 60% of the "
+                             "cycles"},
         "decode": {"value": round(dec_gbps, 1), "unit": "GB/s",
                    "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
                                 "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
