@@ -34,8 +34,7 @@ def _run(cmd):
 
 
 # Per-source extra flags. The forward and backward kernels want the MFMA
-# results that their softmax reads in VGPRs (the VGPR form; the four-wave
-# forward variant keeps O^T in AGPRs through inline asm, and the one-wave dK/dV
+# results that their softmax reads in VGPRs (the VGPR form; the one-wave dK/dV
 # kernel lets the allocator use AGPRs for the rest: measured 2-3% faster than
 # accumulating into AGPRs and copying the scores out). Their copy asm sets M0,
 # which no other instruction of those kernels uses (the warning about
