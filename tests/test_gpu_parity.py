@@ -315,3 +315,12 @@ def test_d64_large_grid_takes_the_eight_wave_path(causal):
     N = 4096 if causal else 4095
     q, k, v = si.random_case(9300 + N, 1, 32, N, 64, "bf16", std=1.5)
     print("d64 eight-wave", causal, _fwd_case(q, k, v, "bf16", causal, fa.default_scale(64)))
+
+
+@pytest.mark.parametrize("B,H,N,causal", [(2, 32, 4096, True), (3, 24, 4000, False)])
+def test_head_grouped_workgroup_order(B, H, N, causal):
+    """With 64 or more heads of 16 or more 256-row query tiles the launcher orders the workgroups in
+    groups of 16 heads (two per XCD at a time); B*H = 72 leaves a short last group of 8 heads. Every
+    element of O and the LSE against the oracle."""
+    q, k, v = si.random_case(9400 + N + B, B, H, N, 128, "bf16", std=1.0)
+    print("grouped order", B, H, N, causal, _fwd_case(q, k, v, "bf16", causal, fa.default_scale(128)))

@@ -299,3 +299,37 @@ def test_paged_decode_splits(page_size, nsplit):
                 assert key // page_size < max_pages
                 covered[key] += 1
         assert (covered[:length] == 1).all()
+
+
+def head_group(NW, BH, n_qt):
+    """The forward launcher's heads per group of the workgroup order (one group: all heads)."""
+    if NW == 8 and ((BH >= 64 and n_qt >= 16) or n_qt >= 128):
+        return min(16, BH)
+    return BH
+
+
+def workgroup_item(i, BH, n_qt, GH):
+    """fwd_bf16_kernel's workgroup -> (head, rank) map for heads in groups of GH."""
+    grp = i // (GH * n_qt)
+    gh = min(GH, BH - grp * GH)
+    r = i - grp * GH * n_qt
+    return grp * GH + r % gh, r // gh
+
+
+@pytest.mark.parametrize("BH", [1, 3, 8, 16, 24, 32, 64, 72, 128, 256])
+@pytest.mark.parametrize("n_qt", [1, 2, 16, 33, 128, 512])
+def test_forward_workgroup_order_is_a_permutation(BH, n_qt):
+    """Every (head, query tile) is taken by exactly one workgroup; in a group of 16 heads workgroup i
+    (which runs on XCD i % 8) takes a head of the group's XCD i % 8 pair, ranks in order."""
+    GH = head_group(8, BH, n_qt)
+    items = [workgroup_item(i, BH, n_qt, GH) for i in range(BH * n_qt)]
+    assert sorted(items) == [(b, r) for b in range(BH) for r in range(n_qt)]
+    if GH == 16:
+        full = (BH // 16) * 16 * n_qt
+        for i in range(full):
+            bh, rank = items[i]
+            assert (bh - 16 * (i // (16 * n_qt))) % 8 == i % 8
+        ranks = [items[i][1] for i in range(16 * n_qt)]
+        assert ranks == sorted(ranks)                 # heaviest (lowest rank) first within a group
+    else:
+        assert items == [(i % BH, i // BH) for i in range(BH * n_qt)]
