@@ -465,22 +465,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void fwd_bf16_kernel(const uint16_
 constexpr int kSmallGridPerCU = 2;
 constexpr int kNumCU = 256;
 
-// Heads per group of the workgroup order. Interleaving all heads (one group)
-// keeps the heaviest causal tiles of every head first, which packs the
-// workgroups best, but each XCD then streams the K/V of BH / 8 heads at once.
-// Where that is 8 heads or more (and heads have 16 or more query tiles), or a
-// head's K/V alone is far beyond an XCD's L2 (128 or more query tiles), groups
-// of 16 heads (two per XCD at a time) let the workgroups of an XCD share K/V
-// tiles in its L2, which is worth more than the packing: measured 2-16% faster
-// over batch 2-8 at 4K-16K and 3-14% at 32K-128K, and 1.4% slower at B=1
-// H=32 N=8K, where one group is kept. The small-grid four-wave path keeps one
-// group: all its workgroups are resident at once, two per CU, and the rank
-// order pairs a heavy with a lighter one on each CU.
-static int head_group(int NW, int BH, int n_qt) {
-  if (NW == 8 && ((BH >= 64 && n_qt >= 16) || n_qt >= 128)) return 16 < BH ? 16 : BH;
-  return BH;
-}
-
 template <int D, int NW, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                     int N, float scale, hipStream_t s) {

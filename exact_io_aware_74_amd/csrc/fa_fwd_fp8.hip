@@ -104,7 +104,7 @@ template <int HD, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
                                                        const uint8_t* __restrict__ V, uint16_t* __restrict__ O,
                                                        float* __restrict__ LSE, int N, float lse_scale, float c2,
-                                                       float v_descale, int n_qt, int BH) {
+                                                       float v_descale, int n_qt, int BH, int GH) {
   using T = Fp8Tile<HD>;
   constexpr int D = T::D;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::NBUF * T::KT];
@@ -112,8 +112,12 @@ __global__ __launch_bounds__(512, 1) void fwd_fp8_kernel(const uint8_t* __restri
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hf = l >> 5, lq = l & 31;
-  const int bh = blockIdx.x % BH;
-  const int rank = blockIdx.x / BH;
+  // heads in groups of GH, each group's query tiles in rank order (see head_group)
+  const int grp = blockIdx.x / (GH * n_qt);
+  const int gh = min(GH, BH - grp * GH);
+  const int r = blockIdx.x - grp * GH * n_qt;
+  const int bh = grp * GH + r % gh;
+  const int rank = r / gh;
   const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
   const int q0 = qt * T::BR;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -398,7 +402,8 @@ static hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, 
   if (!(c2 >= FLT_MIN)) c2 = FLT_MIN;  // as in the bf16 kernel: masked scores stay at probability 0
   const uint8_t *qp = (const uint8_t*)q, *kp = (const uint8_t*)k, *vp = (const uint8_t*)v;
   uint16_t* op = (uint16_t*)o;
-  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &lse_scale, &c2, &v_descale, &n_qt, &BH};
+  int GH = head_group(T::NW, BH, n_qt);
+  void* args[] = {&qp, &kp, &vp, &op, &lse, &N, &lse_scale, &c2, &v_descale, &n_qt, &BH, &GH};
   const void* kern = causal ? (const void*)&fwd_fp8_kernel<D, true> : (const void*)&fwd_fp8_kernel<D, false>;
   return hipLaunchKernel(kern, dim3((unsigned)(n_qt * BH)), dim3(64 * T::NW), args, 0, s);
 }

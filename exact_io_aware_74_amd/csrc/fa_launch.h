@@ -6,6 +6,20 @@
 
 namespace fa {
 
+// Heads per group of the forward kernels' workgroup order, for workgroups of
+// `waves` waves x 32 query rows (n_qt query tiles per head). One group (all
+// heads interleaved) keeps the heaviest causal tiles of every head first,
+// which packs the workgroups best, but each XCD then streams the K/V of BH / 8
+// heads at once. Where that is 8 heads or more (and heads have 16 or more
+// query tiles), or a head's K/V alone is far beyond an XCD's L2 (128 or more
+// query tiles), groups of 16 heads (two per XCD at a time) let the workgroups
+// of an XCD share K/V tiles in its L2. Four-wave workgroups (the small-grid
+// path) keep one group: all of them are resident at once, two per CU.
+inline int head_group(int waves, int BH, int n_qt) {
+  if (waves == 8 && ((BH >= 64 && n_qt >= 16) || n_qt >= 128)) return 16 < BH ? 16 : BH;
+  return BH;
+}
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, bool causal, float scale, hipStream_t s);
 
