@@ -155,7 +155,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                           const float* __restrict__ lse2, const float* __restrict__ Dsum,
                                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
-                                                          int Npad, float scale, float c2, int BH, int causal_flag) {
+                                                          int Npad, float scale, float c2, int BH, int causal_flag,
+                                                          int GH) {
   const bool CAUSAL = causal_flag != 0;
   using T = BwdTile<D>;
   constexpr int SLOT = 2 * T::BYTES + 512;  // Q tile, dO tile, 64 x (LSE2, D) floats
@@ -165,7 +166,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hf = l >> 5, lq = l & 31;
-  const int bh = blockIdx.x % BH, kt = blockIdx.x / BH;  // key tiles of a head in order: heaviest first
+  // heads in groups of GH (see head_group), each group's key tiles in order:
+  // heaviest first
+  const int n_kt = (N + 127) / 128;
+  const int grp = blockIdx.x / (GH * n_kt);
+  const int gh = min(GH, BH - grp * GH);
+  const int rr = blockIdx.x - grp * GH * n_kt;
+  const int bh = grp * GH + rr % gh, kt = rr / gh;
   const int k0 = kt * 128, kw0 = k0 + 32 * w;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = Q + head, *Kh = K + head, *Vh = V + head, *dOh = dO + head;
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
                                                         const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                         const float* __restrict__ lse2, const float* __restrict__ Dsum,
                                                         uint16_t* __restrict__ dQ, int N, int Npad, float scale, float c2,
-                                                        int n_qt, int BH) {
+                                                        int n_qt, int BH, int GH) {
   using T = BwdTile<D>;
   constexpr int SLOT = 2 * T::BYTES;      // K tile, V tile
   constexpr int IPW = 2 * T::NCOPY / 8;   // copy instructions per wave per tile
@@ -423,7 +430,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(const uint16_t* __restri
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hf = l >> 5, lq = l & 31;
-  const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
+  const int grp = blockIdx.x / (GH * n_qt);  // heads in groups of GH (see head_group)
+  const int gh = min(GH, BH - grp * GH);
+  const int rr = blockIdx.x - grp * GH * n_qt;
+  const int bh = grp * GH + rr % gh, rank = rr / gh;
   const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;  // heaviest causal query tiles first
   const int q0 = qt * 256, wq0 = q0 + 32 * w;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -578,13 +588,14 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
 
   dim3 g1((unsigned)(((N + 127) / 128) * BH)), b1(256);
   int causal_flag = CAUSAL ? 1 : 0;
-  void* a1[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dkp, &dvp, &N, &Npad, &scale, &c2, (void*)&BH, &causal_flag};
+  int n_qt = (N + 255) / 256;
+  int GH = head_group(8, BH, n_qt);  // the same sequence-length thresholds as the forward's 256-row tiles
+  void* a1[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dkp, &dvp, &N, &Npad, &scale, &c2, (void*)&BH, &causal_flag, &GH};
   e = hipLaunchKernel((const void*)&bwd_dkdv_kernel<D>, g1, b1, a1, 0, s);
   if (e != hipSuccess) return e;
 
-  int n_qt = (N + 255) / 256;
   dim3 g2((unsigned)(n_qt * BH)), b2(512);
-  void* a2[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dqp, &N, &Npad, &scale, &c2, &n_qt, (void*)&BH};
+  void* a2[] = {&qp, &kp, &vp, &dop, &lse2, &dsum, &dqp, &N, &Npad, &scale, &c2, &n_qt, (void*)&BH, &GH};
   return hipLaunchKernel((const void*)&bwd_dq_kernel<D, CAUSAL>, g2, b2, a2, 0, s);
 }
 
