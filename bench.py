@@ -42,7 +42,7 @@ PREFILL = "bf16_h32_n8192_d128_causal_k2"
 DECODE = "decode_b16h32_l32768_d128"
 LONG = "bf16_b4h32_n131072_d128_causal"
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_n8192.json")
-FWD_SOURCES = [os.path.join(ROOT, "exact_io_aware_74_amd", "csrc", f) for f in ("fa_fwd_bf16.hip", "fa_device.h")]
+FWD_SOURCES = [os.path.join(ROOT, "exact_io_aware_74_amd", "csrc", f) for f in ("fa_fwd_bf16.hip", "fa_device.h", "fa_launch.h")]
 
 
 def fwd_source_digest() -> str:
