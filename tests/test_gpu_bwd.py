@@ -148,3 +148,12 @@ def test_bwd_workload_8k_causal_k2_two_heads():
     q, k, v = (si.tensor_full(w, t) for t in ("q", "k", "v"))
     do = si.upstream_grad(w.wid, w.B, w.H, w.N, w.d, "bf16")
     print(bwd_case(q, k, v, do, True, w.scale, heads=[(0, 0), (0, 31)]))
+
+
+def test_bwd_head_grouped_order():
+    """B=2 H=32 N=4096 causal: 64 heads of 16 query tiles, so both backward kernels take the workgroup
+    order in groups of 16 heads (two per XCD at a time). Whole heads of dQ, dK and dV from both groups,
+    several XCD positions, against the oracle."""
+    q, k, v = si.random_case(4242, 2, 32, 4096, 128, "bf16")
+    do = si.upstream_grad(4243, 2, 32, 4096, 128, "bf16")
+    print(bwd_case(q, k, v, do, True, fa.default_scale(128), heads=[(0, 0), (0, 9), (0, 23), (1, 6), (1, 31)]))

@@ -162,3 +162,13 @@ def test_float8_dtype_accepted():
     a, _ = fa.fwd_fp8(dev8(q8), dev8(k8), dev8(v8), ds)
     b, _ = fa.fwd_fp8(*(dev8(x).view(torch.float8_e4m3fn) for x in (q8, k8, v8)), ds)
     assert torch.equal(a, b)
+
+
+def test_head_grouped_order():
+    """B=2 H=32 N=4096 causal: 64 heads of 16 query tiles take the workgroup order in groups of 16 heads.
+    Whole heads from both groups and several XCD positions against the oracle."""
+    q8, k8, v8, ds = si.fp8_case(4244, 2, 32, 4096, 128)
+    go, ro, gl, rl, vmax = fp8_case_run(q8, k8, v8, ds, True, fa.default_scale(128),
+                                        heads=[(0, 0), (0, 9), (0, 23), (1, 6), (1, 31)])
+    print("fp8 grouped", assert_fp8_close(go, ro, vmax))
+    assert_lse_close(gl, rl, "bf16")
