@@ -16,26 +16,24 @@
 //    workspace (rows padded to a multiple of 64 with zeros). The other two
 //    kernels start each dP accumulation from -D, so the MFMA result is
 //    already dP - D and dS = P * (dP - D) costs one multiply per element;
-//  * bwd_dkdv: one workgroup per 128 keys of a head (4 waves x 32 keys). A
-//    wave keeps its keys' K and V rows in VGPRs as MFMA B operands and streams
-//    64-row Q / dO tiles through LDS. Per 32 queries it recomputes
-//    S = Q K^T and dP = dO V^T (lane l holds key l % 32 and 16 queries), forms
-//    P and dS in registers and accumulates dV += P^T dO and dK += dS^T Q, the
-//    P^T / dS^T operands coming straight from those registers and dO / Q
-//    through the transposing LDS read. With a single wave per SIMD the
-//    kernel pipelines itself: the S / dP MFMAs of the next block (from row
-//    fragments read a block ahead) alternate with forming this block's P and
-//    dS in the wave's instruction stream (fenced groups), and masked scores
-//    are set to -inf up front so that code is straight-line;
+//  * bwd_dkdv: one workgroup per 128 keys of a head, eight waves, two per
+//    SIMD. The two waves of a SIMD own the same 32 keys and take the first
+//    and the second 32-query block of each 64-row Q / dO tile; K and V of the
+//    workgroup's keys stay in LDS as MFMA B operands. Per block a wave
+//    recomputes S = Q K^T and dP = dO V^T (lane l holds key l % 32 and 16
+//    queries), forms P and dS in registers and accumulates dV += P^T dO and
+//    dK += dS^T Q, the P^T / dS^T operands coming straight from those
+//    registers and dO / Q through the transposing LDS read. The second wave
+//    of each pair adds its sums into the first's through LDS at the end;
 //  * bwd_dq: one workgroup per 256 queries (8 waves x 32 rows), laid out like
 //    the forward: S^T = K Q^T and dP^T = V dO^T with Q / dO in VGPRs, then
 //    dQ^T += K^T dS^T with K^T from the transposing read. No atomics: dQ is
 //    owned by one wave, so results are deterministic.
-// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into a ring (three
-// slots for dK / dV, two for dQ; one barrier per tile), row-major by 64-dim
-// octets with the 16-byte chunks XOR-swizzled per row by one function that
-// keeps both the row-fragment reads (16 rows, one chunk) and the transposing
-// reads (4 rows x 4 chunks) free of bank conflicts.
+// Tiles are copied HBM -> LDS with global_load_lds_dwordx4 into a two-slot
+// ring (one barrier per tile), row-major by 64-dim octets with the 16-byte
+// chunks XOR-swizzled per row by one function that keeps both the
+// row-fragment reads (16 rows, one chunk) and the transposing reads (4 rows x
+// 4 chunks) free of bank conflicts.
 #include <float.h>
 
 #include "fa_device.h"
@@ -147,11 +145,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 }
 
 // ---- dK, dV: one workgroup per 128 keys of one head ----
-// Causality is a run-time flag here (uniform branches): the causal and
-// non-causal cases then share one register allocation, which fits without
-// spills.
+// Eight waves, two per SIMD: waves w and w + 4 share a SIMD and the 32 keys
+// k0 + 32 (w % 4) .. + 31, wave w taking the first and wave w + 4 the second
+// 32-query block of every 64-row Q / dO tile. K and V of the workgroup's keys
+// stay in LDS for its lifetime and feed the score MFMAs as B operands, so a
+// wave holds only its dK / dV sums and one block's scores; the two waves of a
+// SIMD hide each other's LDS waits and arithmetic. At the end the second wave
+// of each pair hands its sums to the first through LDS. Causality is a
+// run-time flag here (uniform branches): the causal and non-causal cases then
+// share one register allocation.
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                                                           const float* __restrict__ lse2, const float* __restrict__ Dsum,
                                                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
@@ -160,12 +164,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const bool CAUSAL = causal_flag != 0;
   using T = BwdTile<D>;
   constexpr int SLOT = 2 * T::BYTES + 512;  // Q tile, dO tile, 64 x (LSE2, D) floats
-  constexpr int IPW = 2 * T::NCOPY / 4;     // copy instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * SLOT];
+  constexpr int KVB = 4 * T::BYTES;         // K rows k0 .., k0 + 64 .., then V rows k0 .., k0 + 64 ..
+  constexpr int IPW = 2 * T::NCOPY / 8;     // Q / dO copy instructions per wave per tile
+  constexpr int KV_IPW = 4 * T::NCOPY / 8;  // K / V copy instructions per wave
+  constexpr int MERGE = 4 * 2 * T::NDB * 16 * 64 * 4;  // hand-over: 4 key blocks x (dK, dV) x 64 lanes
+  static_assert(MERGE <= KVB + 2 * SLOT, "hand-over buffer");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[KVB + 2 * SLOT];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, hf = l >> 5, lq = l & 31;
+  const int kb = w & 3, par = w >> 2;  // key block, query block within each tile
   // heads in groups of GH (see head_group), each group's key tiles in order:
   // heaviest first
   const int n_kt = (N + 127) / 128;
@@ -173,28 +182,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const int gh = min(GH, BH - grp * GH);
   const int rr = blockIdx.x - grp * GH * n_kt;
   const int bh = grp * GH + rr % gh, kt = rr / gh;
-  const int k0 = kt * 128, kw0 = k0 + 32 * w;
+  const int k0 = kt * 128, kw0 = k0 + 32 * kb;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = Q + head, *Kh = K + head, *Vh = V + head, *dOh = dO + head;
   const float* L2h = lse2 + (size_t)bh * Npad;
   const float* Dh = Dsum + (size_t)bh * Npad;
 
-  // K and V rows of this wave's keys as B operands: lane (key kw0 + lq, half
-  // hf) holds head dims 16c + 8hf .. + 7
-  bf16x8 kT[T::NC], vT[T::NC];
-  {
-    const int key = kw0 + lq;
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      if (key < N) {
-        kT[c] = *(const bf16x8*)(Kh + (size_t)key * D + 16 * c + 8 * hf);
-        vT[c] = *(const bf16x8*)(Vh + (size_t)key * D + 16 * c + 8 * hf);
-      } else {
-        kT[c] = (bf16x8){};
-        vT[c] = (bf16x8){};
-      }
-    }
-  }
   f32x16 dv[T::NDB], dk[T::NDB];
 #pragma unroll
   for (int db = 0; db < T::NDB; ++db) {
@@ -204,21 +197,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
 
   const TileLanes tl(l);
   const int n_qt = (N + BT - 1) / BT;
-  const int qt0 = CAUSAL ? k0 / BT : 0;  // earlier query tiles see none of these keys
-  const int n_t = n_qt > qt0 ? n_qt - qt0 : 0;  // query tiles this workgroup visits
-  // ring of three slots: tile t (counted from qt0) sits in slot t % 3
+  const int qt0 = CAUSAL ? k0 / BT : 0;         // earlier query tiles see none of these keys
+  const int n_t = n_qt > qt0 ? n_qt - qt0 : 0;  // query tiles this workgroup visits (>= 1)
   uint32_t coff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) coff[i] = copy_off<D>((w * IPW + i) % T::NCOPY, l);
+  // tile t (counted from qt0) into ring slot `slot` (t % 2)
   auto copy = [&](int t, int slot) __attribute__((always_inline)) {
     const int qt = qt0 + t;
-    const uint32_t base = lds_addr(lds) + slot * SLOT;
+    const uint32_t base = lds_addr(lds) + KVB + slot * SLOT;
     if (qt * BT + BT <= N) {
       const uint16_t* qtile = Qh + (size_t)qt * (BT * D);
       const uint16_t* dotile = dOh + (size_t)qt * (BT * D);
 #pragma unroll
       for (int i = 0; i < IPW; ++i) {
-        const int v = w * IPW + i;  // 0 .. NCOPY - 1: Q, then dO
+        const int v = w * IPW + i;  // 0 .. 2 NCOPY - 1: Q, then dO
         if (v < T::NCOPY)
           copy_part_s(qtile, coff[i], base, v);
         else
@@ -239,180 +232,119 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
       global_load_lds16(src, base + 2 * T::BYTES);
     }
   };
-
-  // 32-query block b: rows (qt0 + b/2) * 64 + 32 * (b % 2) .. + 31, in tile
-  // b / 2, whose ring slot the callers pass as a byte offset (tQ)
-  auto blk_q0 = [&](int b) { return (qt0 + (b >> 1)) * BT + 32 * (b & 1); };
-  // Row fragments (A operands of S and dP) of block b. Blocks past the end
-  // read an in-range ring slot; the values are never used.
-  auto read_rows = [&](bf16x8(&rq)[T::NC], bf16x8(&rd)[T::NC], int tQ, int b) __attribute__((always_inline)) {
-    const int h = b & 1;
+  // the workgroup's K and V rows; rows past N repeat the last row, which only
+  // feeds the scores of those keys, whose dK / dV are not written
 #pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      rq[c] = row_frag(lds, tQ, tl, h, c);
-      rd[c] = row_frag(lds, tQ + T::BYTES, tl, h, c);
-    }
-  };
-  // -D of the 32 queries of half hh of the tile at byte offset `tile`, in
-  // accumulator order (element r: query (r%4) + 8(r/4) + 4hf of the half)
-  auto neg_d = [&](int tile, int hh) __attribute__((always_inline)) {
-    const float* st = (const float*)(lds + tile + 2 * T::BYTES) + BT + 32 * hh + 4 * hf;
-    f32x16 r;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 x = *(const f32x4*)(st + 8 * rb);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[4 * rb + i] = x[i];
-    }
-    return r;
-  };
-  // S and dP - D of one block (dP accumulated from -D)
-  auto score = [&](f32x16& sc, f32x16& dp, const bf16x8(&rq)[T::NC], const bf16x8(&rd)[T::NC], const f32x16& nd)
-                   __attribute__((always_inline)) {
-#pragma unroll
-    for (int c = 0; c < T::NC; ++c) {
-      sc = mfma32x32x16(rq[c], kT[c], c == 0 ? (f32x16){} : sc);
-      dp = mfma32x32x16(rd[c], vT[c], c == 0 ? nd : dp);
-    }
-  };
-  // One block b. With one wave per SIMD the wave issues in order, so the
-  // matrix cores only stay busy if MFMAs and arithmetic alternate in its
-  // instruction stream. The block is one straight-line region (masked blocks
-  // first set their hidden scores to -inf in a uniform branch), laid out as:
-  // the LSE / D values of block b and the transposed fragments of its first
-  // 16 queries are read (LDS answers in issue order, so these come first);
-  // the score MFMAs of block b + 1 alternate with forming P and dS of block
-  // b (the row fragments of b + 1 were read one block earlier; past the last
-  // block they score an in-range ring slot nobody uses); the row fragments
-  // of block b + 2 are read into the registers those MFMAs consumed; dV and
-  // dK accumulate.
-  // Lane: key kw0 + lq; element r: query qb0 + (r%4) + 8(r/4) + 4hf.
-  // tQ: ring slot offset of block b's tile; tQ2: that of block b + 2's.
-  auto block = [&](f32x16& sc, f32x16& dp, f32x16& sc_n, f32x16& dp_n, const bf16x8(&rq_n)[T::NC],
-                   const bf16x8(&rd_n)[T::NC], bf16x8(&rq_f)[T::NC], bf16x8(&rd_f)[T::NC], int b, int tQ, int tQ2)
-                   __attribute__((always_inline)) {
-    // A block before the diagonal (causal) or past the last row has every
-    // score masked, so its P and dS are exactly 0 and it adds nothing.
-    const int qb0 = blk_q0(b);
-    if ((qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31)) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
-        if (!(q < N && (!CAUSAL || key <= q))) {
-          sc[r] = -INFINITY;  // P = 0
-          dp[r] = 0.f;        // dS = 0 * 0 = 0 whatever the row data holds
-        }
-      }
-    }
-    const int tdO = tQ + T::BYTES, h = b & 1;
-    const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][-D x 64]
-    auto read_stats = [&](f32x4& L, int rb) __attribute__((always_inline)) {
-      L = *(const f32x4*)(stats + 32 * h + 8 * rb + 4 * hf);
-    };
-    // -D of block b + 1's queries in accumulator order (element r: query
-    // (r%4) + 8(r/4) + 4hf of the block): the starting value of its dP
-    const f32x16 nd_n = neg_d(b & 1 ? tQ2 : tQ, (b + 1) & 1);
-    // Eight groups: the two score MFMAs of head-dim chunk j for block b + 1,
-    // then P and dS of elements 2j, 2j + 1 of block b. The LSE / D values are
-    // read one group pair ahead and the transposed fragments of the first 16
-    // queries during the second half; the fences keep this order and the
-    // register pressure of source order.
-    f32x4 L4[2];
-    bf16x8 tq[T::NDB], td[T::NDB];  // transposed fragments of one 16-query half (kc)
-    bf16x8 pb[2], sb[2];
-    read_stats(L4[0], 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rb = j >> 1, e = 2 * (j & 1), r = 2 * j;
-      if ((j & 1) == 0 && rb < 3) read_stats(L4[(rb + 1) & 1], rb + 1);
-      if (j >= 8 - T::NDB) {
-        const int db = j - (8 - T::NDB);
-        td[db] = tr_frag(lds, tdO, tl, h, 0, db);
-        tq[db] = tr_frag(lds, tQ, tl, h, 0, db);
-      }
-      if (j < T::NC) {
-        sc_n = mfma32x32x16(rq_n[j], kT[j], j == 0 ? (f32x16){} : sc_n);
-        dp_n = mfma32x32x16(rd_n[j], vT[j], j == 0 ? nd_n : dp_n);
-      }
-      const f32x4 L = L4[rb & 1];
-      const float p0 = fast_exp2(fmaf(sc[r], c2, -L[e]));
-      const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
-      const float d0 = p0 * dp[r], d1 = p1 * dp[r + 1];  // dp already holds dP - D
-      const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(d0, d1);
-      pb[r >> 3][r & 7] = pp[0];
-      pb[r >> 3][(r & 7) + 1] = pp[1];
-      sb[r >> 3][r & 7] = ss[0];
-      sb[r >> 3][(r & 7) + 1] = ss[1];
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int c = 8; c < T::NC; ++c) {  // head dims past 128 (none at d = 128)
-      sc_n = mfma32x32x16(rq_n[c], kT[c], sc_n);
-      dp_n = mfma32x32x16(rd_n[c], vT[c], dp_n);
-    }
-    read_rows(rq_f, rd_f, tQ2, b + 2);
-    // dV += P^T dO and dK += dS^T Q: A = P^T / dS^T (lane: key row, k-slots:
-    // the lane's queries), B = dO / Q through the transposing read
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      if (kc == 1) {
-#pragma unroll
-        for (int db = 0; db < T::NDB; ++db) {
-          td[db] = tr_frag(lds, tdO, tl, h, 1, db);
-          tq[db] = tr_frag(lds, tQ, tl, h, 1, db);
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < T::NDB; ++db) {
-        dv[db] = mfma32x32x16(pb[kc], td[db], dv[db]);
-        dk[db] = mfma32x32x16(sb[kc], tq[db], dk[db]);
-      }
-    }
-  };
-
-  // Tile t + 1 is resident while tile t is processed (block 2t + 1 reads the
-  // rows of the first block of tile t + 1); tile t + 2 is copied during tile
-  // t into the slot of tile t - 1 and published by the barrier that ends t.
-  if (n_t > 0) copy(0, 0);
-  if (n_t > 1) copy(1, 1);
+  for (int i = 0; i < KV_IPW; ++i) {
+    const int v = w * KV_IPW + i, tile = v / T::NCOPY, part = v % T::NCOPY;
+    copy_part<D>(tile < 2 ? Kh : Vh, k0 + 64 * (tile & 1), N, lds_addr(lds) + tile * T::BYTES, part, l);
+  }
+  copy(0, 0);
   wait_vmcnt<0>();
   __syncthreads();
-  f32x16 scA, dpA, scB, dpB;
-  bf16x8 rqA[T::NC], rdA[T::NC], rqB[T::NC], rdB[T::NC];
-  read_rows(rqA, rdA, 0, 0);
-  score(scA, dpA, rqA, rdA, neg_d(0, 0));
-  read_rows(rqB, rdB, 0, 1);
-  // tile t in ring slot s (= t % 3); the next tile in s1, the copy target s2
-  auto tile = [&](int t, int s, int s1, int s2) __attribute__((always_inline)) {
-    if (t + 2 < n_t) copy(t + 2, s2);
-    block(scA, dpA, scB, dpB, rqB, rdB, rqA, rdA, 2 * t, s * SLOT, s1 * SLOT);
-    block(scB, dpB, scA, dpA, rqA, rdA, rqB, rdB, 2 * t + 1, s * SLOT, s1 * SLOT);
+  if (n_t > 1) copy(1, 1);
+
+  // this wave's keys: rows 32 (kb % 2) .. of K / V tile kb / 2
+  const int tK = (kb >> 1) * T::BYTES, tV = 2 * T::BYTES + tK, hk = kb & 1;
+  for (int t = 0; t < n_t; ++t) {
+    const int tQ = KVB + (t & 1) * SLOT, tdO = tQ + T::BYTES;
+    // Block: queries qb0 .. qb0 + 31. Lane: key kw0 + lq; accumulator element
+    // r: query qb0 + (r%4) + 8(r/4) + 4hf. A block wholly before this wave's
+    // keys (causal) or past the last row adds exactly zero and is skipped.
+    const int qb0 = (qt0 + t) * BT + 32 * par;
+    if (qb0 < N && !(CAUSAL && qb0 + 31 < kw0)) {
+      // -D of the block's queries in accumulator order: the starting value of
+      // dP, so the MFMA result is already dP - D
+      f32x16 dp;
+      {
+        const float* st = (const float*)(lds + tQ + 2 * T::BYTES) + BT + 32 * par + 4 * hf;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const f32x4 x = *(const f32x4*)(st + 8 * rb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dp[4 * rb + i] = x[i];
+        }
+      }
+      // S = Q K^T and dP - D = dO V^T - D over the head dim
+      f32x16 sc = (f32x16){};
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c) {
+        sc = mfma32x32x16(row_frag(lds, tQ, tl, par, c), row_frag(lds, tK, tl, hk, c), sc);
+        dp = mfma32x32x16(row_frag(lds, tdO, tl, par, c), row_frag(lds, tV, tl, hk, c), dp);
+      }
+      if ((qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
+          if (!(q < N && (!CAUSAL || key <= q))) {
+            sc[r] = -INFINITY;  // P = 0
+            dp[r] = 0.f;        // dS = 0 * 0 = 0 whatever the row data holds
+          }
+        }
+      }
+      // P = exp2(S c2 - LSE2) and dS = P (dP - D), packed as the bf16 A
+      // operands of the next MFMAs (k-slots: the lane's queries)
+      const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][-D x 64]
+      bf16x8 pb[2], sb[2];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 L = *(const f32x4*)(stats + 32 * par + 8 * rb + 4 * hf);
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const int r = 4 * rb + e;
+          const float p0 = fast_exp2(fmaf(sc[r], c2, -L[e]));
+          const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
+          const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(p0 * dp[r], p1 * dp[r + 1]);
+          pb[r >> 3][r & 7] = pp[0];
+          pb[r >> 3][(r & 7) + 1] = pp[1];
+          sb[r >> 3][r & 7] = ss[0];
+          sb[r >> 3][(r & 7) + 1] = ss[1];
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q, dO / Q through the transposing read
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) {
+          dv[db] = mfma32x32x16(pb[kc], tr_frag(lds, tdO, tl, par, kc, db), dv[db]);
+          dk[db] = mfma32x32x16(sb[kc], tr_frag(lds, tQ, tl, par, kc, db), dk[db]);
+        }
+    }
+    // end of tile t: tile t + 1 has landed for every wave and every wave is
+    // done with tile t, whose slot then receives tile t + 2
     wait_vmcnt<0>();
     __syncthreads();
-  };
-  // Unrolled over the ring depth (t is a multiple of 3 at the top), so every
-  // slot offset is a compile-time constant folded into the LDS instructions.
-  int t = 0;
-  for (; t + 3 <= n_t; t += 3) {
-    tile(t, 0, 1, 2);
-    tile(t + 1, 1, 2, 0);
-    tile(t + 2, 2, 0, 1);
+    if (t + 2 < n_t) copy(t + 2, t & 1);
   }
-  for (; t < n_t; ++t) tile(t, t % 3, (t + 1) % 3, (t + 2) % 3);
 
-  // lane l holds head dim 32*db + lq of keys kw0 + (r%4) + 8(r/4) + 4hf
+  // the second wave of each pair hands its sums to the first (the last
+  // barrier above ended every read of the ring and of K / V)
+  float* hand = (float*)lds;
+  auto at = [&](int which, int db, int r) { return (((kb * 2 + which) * T::NDB + db) * 16 + r) * 64 + l; };
+  if (par == 1) {
 #pragma unroll
-  for (int db = 0; db < T::NDB; ++db)
+    for (int db = 0; db < T::NDB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw0 + (r & 3) + 8 * (r >> 2) + 4 * hf;
-      if (key < N) {
-        const size_t off = head + (size_t)key * D + 32 * db + lq;
-        dV[off] = to_bf16_bits(dv[db][r]);
-        dK[off] = to_bf16_bits(dk[db][r] * scale);
+      for (int r = 0; r < 16; ++r) {
+        hand[at(0, db, r)] = dk[db][r];
+        hand[at(1, db, r)] = dv[db][r];
       }
-    }
+  }
+  __syncthreads();
+  if (par == 0) {
+    // lane l holds head dim 32*db + lq of keys kw0 + (r%4) + 8(r/4) + 4hf
+#pragma unroll
+    for (int db = 0; db < T::NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw0 + (r & 3) + 8 * (r >> 2) + 4 * hf;
+        if (key < N) {
+          const size_t off = head + (size_t)key * D + 32 * db + lq;
+          dV[off] = to_bf16_bits(dv[db][r] + hand[at(1, db, r)]);
+          dK[off] = to_bf16_bits((dk[db][r] + hand[at(0, db, r)]) * scale);
+        }
+      }
+  }
 }
 
 // ---- dQ: one workgroup per 256 queries of one head ----
@@ -586,7 +518,7 @@ hipError_t launch_bwd_t(const void* q, const void* k, const void* v, const void*
   hipError_t e = hipLaunchKernel((const void*)&bwd_prep_kernel<D>, g0, b0, a0, 0, s);
   if (e != hipSuccess) return e;
 
-  dim3 g1((unsigned)(((N + 127) / 128) * BH)), b1(256);
+  dim3 g1((unsigned)(((N + 127) / 128) * BH)), b1(512);
   int causal_flag = CAUSAL ? 1 : 0;
   int n_qt = (N + 255) / 256;
   int GH = head_group(8, BH, n_qt);  // the same sequence-length thresholds as the forward's 256-row tiles

@@ -138,11 +138,26 @@ def fwd_fp8_model(N, causal):
     return cover
 
 
+def bwd_dkdv_ring(n_t):
+    """The dK/dV kernel's two-slot Q/dO ring: tile 0 is copied and published before the loop,
+    tile 1 copied; tile t sits in slot t % 2 and is read during step t; the step ends with a
+    full wait (tile t + 1 lands) and a barrier, after which tile t + 2 is copied into slot t % 2."""
+    slot, published = {0: 0}, {0}
+    if n_t > 1:
+        slot[1] = 1
+    for t in range(n_t):
+        assert slot[t % 2] == t and t in published
+        published |= {slot[s] for s in slot}
+        if t + 2 < n_t:
+            slot[t % 2] = t + 2
+
+
 def bwd_dkdv_model(N, causal):
-    """bwd_dkdv_kernel: 128-key workgroups, 32 keys per wave, 32-query blocks of 64-row tiles
-    from query tile k0 / 64 on (causal). Every block of the visited tiles is computed; a block
-    with no visible pair (before the diagonal, or past the last row) must take the masked path,
-    which zeroes all of its probabilities."""
+    """bwd_dkdv_kernel: 128-key workgroups of eight waves; wave w owns keys k0 + 32 (w % 4) ..
+    + 31 and the query block 32 (w // 4) of every 64-row tile from query tile k0 / 64 on (causal).
+    A block with no visible pair (before the wave's keys, or past the last row) is skipped; a
+    block that needs the mask takes the masked path, which zeroes its hidden probabilities. The
+    two waves of a key block cover the two halves of each tile; their sums are added at the end."""
     BT = 64
     cover = np.zeros((N, N), dtype=np.int64)
     n_qt = math.ceil(N / BT)
@@ -150,22 +165,24 @@ def bwd_dkdv_model(N, causal):
         k0 = kt * 128
         qt0 = k0 // BT if causal else 0
         n_t = max(n_qt - qt0, 0)
-        for w in range(4):
-            kw0 = k0 + 32 * w
+        assert n_t >= 1
+        bwd_dkdv_ring(n_t)
+        for w in range(8):
+            kb, par = w % 4, w // 4
+            kw0 = k0 + 32 * kb
             c0, c1 = kw0, min(kw0 + 32, N)
-            if c0 >= N:
-                continue
-            for b in range(2 * n_t):
-                qb0 = (qt0 + b // 2) * BT + 32 * (b % 2)
-                valid = qb0 < N and (not causal or qb0 + 31 >= kw0)
-                vis = visible(N, causal)[qb0:min(qb0 + 32, N), c0:c1] if qb0 < N else np.zeros((0, 0), bool)
+            for t in range(n_t):
+                qb0 = (qt0 + t) * BT + 32 * par
+                active = qb0 < N and not (causal and qb0 + 31 < kw0)
+                vis = visible(N, causal)[qb0:min(qb0 + 32, N), c0:c1] if qb0 < N and c0 < N else np.zeros((0, 0), bool)
                 need_mask = (qb0 + 32 > N) or (causal and qb0 < kw0 + 31)
-                if not valid:
-                    assert not vis.any() and need_mask
+                if not active:
+                    assert not vis.any()
                     continue
                 if not need_mask:
                     assert vis.all()
-                cover[qb0:min(qb0 + 32, N), c0:c1] += vis
+                if c0 < N:  # the sums of keys past N are not written
+                    cover[qb0:min(qb0 + 32, N), c0:c1] += vis
     return cover
 
 
