@@ -234,7 +234,7 @@ def test_pins_catch_planted_mistake(kind):
             ok = False
         if not ok:
             caught.append(p.__name__)
-    assert caught, f"no pin catches the mistake {kind}"
+    assert len(caught) >= 4, f"fewer than four pins catch the mistake {kind}: {caught}"
 
 
 def test_unmutated_copy_passes():
