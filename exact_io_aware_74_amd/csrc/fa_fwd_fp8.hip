@@ -34,7 +34,11 @@
 //    with unit u's probabilities between them (unit u's V^T reads in flight
 //    meanwhile), then the P V MFMAs of unit u with the K reads of unit u + 2
 //    in flight and unit u + 1's row maximum and reference update after them,
-//    so every unit's reference is settled before its probabilities are taken.
+//    so every unit's reference is settled before its probabilities are taken;
+//  * as in the bf16 kernel: each SIMD holds one low and one high row block,
+//    the last tiles run without barriers once every copy is in, the score
+//    MFMA stretch runs at raised wave priority, and workgroups take heads in
+//    groups (head_group) with the heaviest causal query tiles first.
 #include <float.h>
 
 #include "fa_device.h"
