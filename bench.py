@@ -528,7 +528,10 @@ def summarize_pmc(root: str) -> str:
     where their counters were taken: clock = GRBM_GUI_ACTIVE / 8 XCDs / dispatch time; MFMA busy =
     SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / clock cycles; VALU per MFMA = (SQ_INSTS_VALU -
     SQ_INSTS_MFMA) / SQ_INSTS_MFMA; HBM bytes = FETCH_SIZE and WRITE_SIZE KiB x 1024, each scaled by
-    the 1 GiB copy of its run (bench.py --copy-calibration)."""
+    the 1 GiB copy of its run (bench.py --copy-calibration). Where a pass took SQ_WAVE_CYCLES, a second
+    table gives per-SIMD fractions of the clock cycles (MFMA busy; MFMA and VALU executing together,
+    SQ_VALU_MFMA_COEXEC_CYCLES) and per-wave fractions of the wave cycles (SQ_WAIT_ANY, SQ_WAIT_INST_ANY,
+    SQ_WAIT_INST_LDS, SQ_ACTIVE_INST_ANY over SQ_WAVE_CYCLES, which count in the same units)."""
     import csv
     import glob
     per, times = {}, {}
@@ -571,6 +574,22 @@ def summarize_pmc(root: str) -> str:
                      f"{f(c['SQ_INSTS_LDS'] / 1e6 if 'SQ_INSTS_LDS' in c else None, '{:.1f}')} | "
                      f"{f(c['SQ_LDS_BANK_CONFLICT'] / 1e6 if 'SQ_LDS_BANK_CONFLICT' in c else None, '{:.2f}')} | "
                      f"{f(c.get('FETCH_SIZE'), '{:.4g}')} | {f(c.get('WRITE_SIZE'), '{:.4g}')} |")
+    # where a pass took the wave-state counters: what the SIMDs and waves spend their cycles on
+    stall = [(kg, cs) for kg, cs in per.items() if "SQ_WAVE_CYCLES" in cs]
+    if stall:
+        lines += ["", "| kernel | grid (threads) | MFMA busy | MFMA and VALU together | waves waiting (any) "
+                  "| waves waiting to issue | waves waiting to issue LDS | waves issuing |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for (k, g), cs in sorted(stall, key=lambda kv: -avg(times[kv[0]])):
+            c = {n: avg(v) for n, v in cs.items()}
+            cyc = c.get("GRBM_GUI_ACTIVE", 0) / 8
+            simd = lambda n: c[n] / 1024 / cyc if cyc and n in c else None
+            wave = lambda n: c[n] / c["SQ_WAVE_CYCLES"] if n in c and c["SQ_WAVE_CYCLES"] else None
+            f = lambda x: "{:.1%}".format(x) if x is not None else "-"
+            lines.append(f"| `{k}` | {g} | {f(simd('SQ_VALU_MFMA_BUSY_CYCLES'))} | "
+                         f"{f(simd('SQ_VALU_MFMA_COEXEC_CYCLES'))} | {f(wave('SQ_WAIT_ANY'))} | "
+                         f"{f(wave('SQ_WAIT_INST_ANY'))} | {f(wave('SQ_WAIT_INST_LDS'))} | "
+                         f"{f(wave('SQ_ACTIVE_INST_ANY'))} |")
     return "\n".join(lines)
 
 
