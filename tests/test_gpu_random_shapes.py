@@ -1,0 +1,90 @@
+"""Seeded random shapes for every entry point against the fp64 oracle, at the
+parity bounds of the fixed-shape tests. The shapes are drawn once from a fixed
+seed (sizes, head counts, head dims, causality, cache lengths, page sizes,
+split counts), so a run is reproducible and a failure names its case. Query
+and key spreads stay within the configured workloads' logit range (q, k ~
+std * N(0,1) with std <= sqrt(2), i.e. logits of standard deviation <= 2, as
+in the 8K workload with K x 2)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from exact_io_aware_74_amd import binding as fa
+from helpers import assert_close, assert_lse_close, to_device, to_f64
+from test_gpu_bwd import assert_grad_close
+from test_gpu_fp8 import assert_fp8_close, fp8_case_run
+from test_gpu_paged import oracle_paged, paged_case, run_paged
+
+pytestmark = pytest.mark.gpu
+
+_rng = np.random.default_rng(20261203)
+STDS = (0.5, 1.0, math.sqrt(2.0))
+
+
+def _draw(n, fn):
+    return [fn(i) for i in range(n)]
+
+
+FWD = _draw(24, lambda i: (int(_rng.integers(1, 4)), int(_rng.integers(1, 6)), int(_rng.integers(1, 2600)),
+                           int(_rng.choice([64, 128])), bool(_rng.integers(0, 2)), float(_rng.choice(STDS)), 100 + i))
+BWD = _draw(12, lambda i: (int(_rng.integers(1, 3)), int(_rng.integers(1, 4)), int(_rng.integers(1, 1100)),
+                           int(_rng.choice([64, 128])), bool(_rng.integers(0, 2)), float(_rng.choice(STDS)), 200 + i))
+DEC = _draw(12, lambda i: (int(_rng.integers(1, 5)), int(_rng.integers(1, 9)), int(_rng.integers(1, 20000)),
+                           int(_rng.choice([64, 128])), int(_rng.integers(1, 300)), 300 + i))
+PAGED = _draw(8, lambda i: (int(_rng.integers(1, 6)), int(_rng.integers(1, 5)), int(_rng.integers(1, 5000)),
+                            int(_rng.choice([64, 128])), int(_rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256])),
+                            int(_rng.integers(1, 200)), 400 + i))
+FP8 = _draw(8, lambda i: (int(_rng.integers(1, 3)), int(_rng.integers(1, 4)), int(_rng.integers(1, 1600)),
+                          int(_rng.choice([64, 128])), bool(_rng.integers(0, 2)), 500 + i))
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,std,seed", FWD)
+def test_forward(B, H, N, d, causal, std, seed):
+    q, k, v = si.random_case(seed, B, H, N, d, "bf16", std=std)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(*(to_device(x, "bf16") for x in (q, k, v)), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O, L = oracle.attention(*(si.as_float64(x, "bf16") for x in (q, k, v)), causal, scale)
+    assert_close(to_f64(o), O, "bf16")
+    assert_lse_close(to_f64(lse), L, "bf16")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,std,seed", BWD)
+def test_backward(B, H, N, d, causal, std, seed):
+    q, k, v = si.random_case(seed, B, H, N, d, "bf16", std=std)
+    do = si.upstream_grad(seed, B, H, N, d, "bf16")
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = (to_device(x, "bf16") for x in (q, k, v, do))
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+    grads = fa.bwd(qd, kd, vd, o, dod, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_grad(*(si.as_float64(x, "bf16") for x in (q, k, v, do)), causal, scale)
+    for got, r, what in zip(grads, ref, ("dQ", "dK", "dV")):
+        assert_grad_close(to_f64(got), r, what, n_rows=N)
+
+
+@pytest.mark.parametrize("B,H,L,d,nsplit,seed", DEC)
+def test_decode(B, H, L, d, nsplit, seed):
+    q, k, v = si.random_case(seed, B, H, 1, d, "bf16", nk=L)
+    o = fa.decode(to_device(q[:, :, 0], "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), nsplit=nsplit)
+    torch.cuda.synchronize()
+    O, _ = oracle.decode(*(si.as_float64(x, "bf16") for x in (q, k, v)))
+    assert_close(to_f64(o), O, "bf16")
+
+
+@pytest.mark.parametrize("B,H,L,d,page_size,nsplit,seed", PAGED)
+def test_paged_decode(B, H, L, d, page_size, nsplit, seed):
+    q, kp, vp, table, lens = paged_case(seed, B, H, L, d, page_size)
+    assert_close(run_paged(q, kp, vp, table, lens, nsplit), oracle_paged(q, kp, vp, table, lens), "bf16")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,seed", FP8)
+def test_fp8_forward(B, H, N, d, causal, seed):
+    q8, k8, v8, ds = si.fp8_case(seed, B, H, N, d)
+    got_o, ref_o, got_l, ref_l, vmax = fp8_case_run(q8, k8, v8, ds, causal, 1.0 / math.sqrt(d))
+    assert_fp8_close(got_o, ref_o, vmax)
+    assert_lse_close(got_l, ref_l, "bf16")
