@@ -99,7 +99,7 @@ int fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* 
  * are rounded to e4m3 (nearest even, after an exact power-of-two scaling that
  * keeps them in e4m3's normal range) for the P V product; the row sums use
  * the fp32 probabilities; O is rounded once to bf16. Each probability carries
- * a relative error of at most 2^-4, so |O - exact| <= (2^-4 + 2^-9) max|V|.
+ * a relative error of at most 2^-4, so |O - exact| <= (2^-4 + 2^-8) max|V|.
  * Errors and alignment as fa_fwd.
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -3,12 +3,12 @@ gradients, element by element on seeded inputs. The forward that produces O and
 LSE is the library's own fa_fwd, as in training.
 
 Tolerance (bf16 inputs and outputs, no figure on the pages or in the targets):
-P and dS enter the MFMAs rounded to bf16 (relative error 2^-9 each, random
-signs) and every gradient is rounded once to bf16 (2^-9), so the normwise error
+P and dS enter the MFMAs rounded to bf16 (relative error up to 2^-8 each,
+random signs) and every gradient is rounded once to bf16 (2^-8), so the normwise error
 is a few 1e-3; the bounds below are relative L2 <= 1e-2 and max |error| <= 2%
 of the tensor's largest reference magnitude. With very few visible keys one
 more term dominates: D = rowsum(dO * O) is formed from the forward's bf16 O,
-and dP - D cancels when a row has one or two keys, so the O rounding (2^-9)
+and dP - D cancels when a row has one or two keys, so the O rounding (2^-8)
 is amplified; a numpy emulation of exactly these roundings gives up to 1.5e-2
 at N = 2 and at most 2.9e-3 from N = 17 on. Below 16 rows the bounds are
 therefore 3e-2 and 6%. Gradients that vanish exactly (dQ and dK with a single

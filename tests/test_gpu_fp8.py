@@ -8,7 +8,7 @@ mantissa bits, relative rounding error at most 2^-4, after an exact
 power-of-two scaling that keeps them normal down to 2^-12 of the row
 reference), the row sums use the unrounded fp32 probabilities, and O is
 rounded once to bf16. Every output element therefore satisfies
-|O - exact| <= (2^-4 + 2^-9) * max|V| (the fp32 accumulation adds far less):
+|O - exact| <= (2^-4 + 2^-8) * max|V| (the fp32 accumulation adds far less):
 the max-abs bound below is 0.07 * max|V|. With random-sign rounding errors
 the normwise error is about 2^-4 / sqrt(3) times a factor below 1; a numpy
 emulation of these roundings gives relative L2 errors of 0.5 % (peaked rows)
