@@ -250,8 +250,11 @@ def decode_workspace_bytes(B: int, H: int, Lkv: int, d: int, nsplit: int) -> int
     return int(load().fa_decode_workspace_bytes(B, H, Lkv, d, nsplit))
 
 
-def naive_fwd(q, k, v, causal: bool = False, scale: float | None = None, workspace=None):
-    """The three-kernel ablation (S and P materialised in HBM). bf16 q, k, v. Returns (o, lse)."""
+def naive_fwd(q, k, v, causal: bool = False, scale: float | None = None, workspace=None, out=None, lse=None):
+    """The three-kernel ablation (S and P materialised in HBM). bf16 q, k, v. Returns (o, lse).
+
+    ``out`` and ``lse`` may pass preallocated outputs, ``workspace`` a float32 device buffer of at least
+    naive_workspace_bytes(B, H, N) bytes."""
     lib = load()
     _check_qkv(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -261,8 +264,13 @@ def naive_fwd(q, k, v, causal: bool = False, scale: float | None = None, workspa
     need = naive_workspace_bytes(B, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 4) // 4, dtype=torch.float32, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    if o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous() or o.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
     with torch.cuda.device(q.device):
         st = lib.fa_naive_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, int(bool(causal)), scale,
                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q))
