@@ -213,12 +213,66 @@ def bwd_dq_model(N, causal):
     return cover
 
 
+def fwd_f32_model(N, causal):
+    """fwd_f32_kernel: four query rows per workgroup (one per wave), 64-key tiles loaded up to the
+    workgroup's last row (causal) or to N; each lane scores one key of the tile, kept iff key < N and
+    (non-causal or key <= row); rows past N write nothing."""
+    cover = np.zeros((N, N), dtype=np.int64)
+    lanes = np.arange(64)
+    for qt in range(math.ceil(N / 4)):
+        q0 = 4 * qt
+        kv_end = min(N, q0 + 4) if causal else N
+        n_tiles = math.ceil(kv_end / 64)
+        for w in range(4):
+            row = q0 + w
+            for t in range(n_tiles):
+                keys = 64 * t + lanes
+                vis = (keys < N) & ((keys <= row) if causal else True)
+                if row < N:
+                    cover[row, keys[vis]] += 1
+            if row < N:                               # every visible key of the row lies in a loaded tile
+                assert (row + 1 if causal else N) <= 64 * n_tiles
+    return cover
+
+
+def fwd_f32_split_model(N, causal, W=4):
+    """fwd_f32_split_kernel: one query row per workgroup; wave w takes the 64-key tiles w, w + W, ...
+    up to the row's last visible key; a lane's key is kept iff key < kv_end, its K row is read at
+    that key (else at key 0), and the P V loop runs over the tile's first nk = min(64, kv_end - 64 t)
+    keys, which must be exactly the kept ones. Wave 0 always holds tile 0, so the merged maximum is
+    finite."""
+    cover = np.zeros((N, N), dtype=np.int64)
+    lanes = np.arange(64)
+    for row in range(N):
+        kv_end = row + 1 if causal else N
+        n_tiles = math.ceil(kv_end / 64)
+        per_wave = [list(range(w, n_tiles, W)) for w in range(W)]
+        assert sorted(t for ts in per_wave for t in ts) == list(range(n_tiles))
+        assert per_wave[0][:1] == [0]
+        for ts in per_wave:
+            for t in ts:
+                keys = 64 * t + lanes
+                vis = keys < kv_end
+                assert np.where(vis, keys, 0).max() < N                 # K reads in bounds
+                nk = min(64, kv_end - 64 * t)
+                assert 1 <= nk <= 64 and np.array_equal(vis, lanes < nk)  # V reads = the kept keys
+                cover[row, keys[vis]] += 1
+    return cover
+
+
 @pytest.mark.parametrize("NW", [8, 4])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", SIZES)
 def test_forward_bf16_tiles(N, causal, NW):
     cover, _ = fwd_bf16_model(N, causal, NW)
     check_cover(cover, N, causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", SIZES)
+def test_forward_f32_tiles(N, causal):
+    check_cover(fwd_f32_model(N, causal), N, causal)
+    check_cover(fwd_f32_split_model(N, causal), N, causal)
 
 
 @pytest.mark.parametrize("n_kt", list(range(1, 40)))
