@@ -4,7 +4,8 @@ seed (sizes, head counts, head dims, causality, cache lengths, page sizes,
 split counts), so a run is reproducible and a failure names its case. Query
 and key spreads stay within the configured workloads' logit range (q, k ~
 std * N(0,1) with std <= sqrt(2), i.e. logits of standard deviation <= 2, as
-in the 8K workload with K x 2)."""
+in the 8K workload with K x 2). A last test runs a longer seeded stream of such
+cases until a time budget is spent."""
 import math
 
 import numpy as np
@@ -88,3 +89,46 @@ def test_fp8_forward(B, H, N, d, causal, seed):
     got_o, ref_o, got_l, ref_l, vmax = fp8_case_run(q8, k8, v8, ds, causal, 1.0 / math.sqrt(d))
     assert_fp8_close(got_o, ref_o, vmax)
     assert_lse_close(got_l, ref_l, "bf16")
+
+
+def test_fuzz_every_entry_point():
+    """A longer seeded stream of random cases over all five entry points, run until a time budget is
+    spent: FA_FUZZ_SEED (default 777) fixes the sequence of cases, FA_FUZZ_SECONDS (default 30) how far
+    into it the run goes. Every case is checked as above; failures are collected and reported together,
+    each with the arguments that reproduce it."""
+    import os
+    import time
+    seed = int(os.environ.get("FA_FUZZ_SEED", "777"))
+    budget = float(os.environ.get("FA_FUZZ_SECONDS", "30"))
+    rng = np.random.default_rng(seed)
+    kinds = ["fwd"] * 5 + ["bwd"] * 2 + ["dec"] * 2 + ["paged"] * 2 + ["fp8"] * 2
+    counts, fails, n, t0 = {}, [], 0, time.time()
+    while time.time() - t0 < budget:
+        kind = kinds[int(rng.integers(0, len(kinds)))]
+        s = 10000 + n
+        if kind == "fwd":
+            fn, args = test_forward, (int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 1500)),
+                                      int(rng.choice([64, 128])), bool(rng.integers(0, 2)), float(rng.choice(STDS)), s)
+        elif kind == "bwd":
+            fn, args = test_backward, (int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 700)),
+                                       int(rng.choice([64, 128])), bool(rng.integers(0, 2)), float(rng.choice(STDS)), s)
+        elif kind == "dec":
+            fn, args = test_decode, (int(rng.integers(1, 5)), int(rng.integers(1, 9)), int(rng.integers(1, 20000)),
+                                     int(rng.choice([64, 128])), int(rng.integers(1, 300)), s)
+        elif kind == "paged":
+            fn, args = test_paged_decode, (int(rng.integers(1, 6)), int(rng.integers(1, 5)), int(rng.integers(1, 5000)),
+                                           int(rng.choice([64, 128])),
+                                           int(rng.choice([1, 2, 4, 8, 16, 32, 64, 128, 256])),
+                                           int(rng.integers(1, 200)), s)
+        else:
+            fn, args = test_fp8_forward, (int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 1200)),
+                                          int(rng.choice([64, 128])), bool(rng.integers(0, 2)), s)
+        try:
+            fn(*args)
+        except AssertionError as e:
+            fails.append(f"{fn.__name__}{args}: {str(e).splitlines()[0]}")
+        counts[kind] = counts.get(kind, 0) + 1
+        n += 1
+    print(f"fuzz seed {seed}: {n} cases in {time.time() - t0:.0f} s {counts}")
+    assert n > 0
+    assert not fails, f"{len(fails)} of {n} cases failed:\n" + "\n".join(fails)
