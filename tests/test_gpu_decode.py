@@ -116,3 +116,18 @@ def test_shutdown_then_decode_again():
         again = fa.decode(qd, kd, vd, nsplit=16)
         torch.cuda.synchronize()
         assert torch.equal(first, again)
+
+
+@pytest.mark.timeout(600)
+def test_one_long_sequence():
+    """One head with a 2,097,929-key cache (d = 128): 64 splits of 32,781 keys (256 batches per workgroup)
+    and a single split over every key (one workgroup, 16,391 batches), both against the oracle."""
+    L, d = (1 << 21) + 777, 128
+    q, k, v = si.random_case(23, 1, 1, 1, d, "bf16", nk=L)
+    qd = to_device(q[:, :, 0, :], "bf16")
+    kd, vd = to_device(k, "bf16"), to_device(v, "bf16")
+    outs = {ns: to_f64(fa.decode(qd, kd, vd, nsplit=ns)) for ns in (64, 1)}
+    del kd, vd
+    ref, _ = oracle.decode(si.as_float64(q, "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
+    for ns, got in outs.items():
+        print("long sequence, nsplit", ns, assert_close(got, ref, "bf16"))
