@@ -128,3 +128,13 @@ def test_workload_decode_b16h32_l32768_paged_sampled_heads():
         got.append(got_all[b, h])
         ref.append(r[0, 0])
     print("paged decode full-size", assert_close(np.stack(got), np.stack(ref), "bf16"))
+
+
+@pytest.mark.timeout(600)
+def test_long_sequences_in_large_pages():
+    """Two sequences of 1,048,909 and 300,001 keys (d = 128) in 64-key pages of a shuffled pool,
+    64 splits (16,390 keys each, so the shorter sequence's last splits are empty), against the oracle."""
+    Lmax = (1 << 20) + 333
+    q, kp, vp, table, lens = paged_case(81, 2, 1, Lmax, 128, 64, lens=[Lmax, 300001])
+    got = run_paged(q, kp, vp, table, lens, 64)
+    print("paged long sequences", assert_close(got, oracle_paged(q, kp, vp, table, lens), "bf16"))
