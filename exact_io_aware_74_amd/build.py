@@ -40,8 +40,8 @@ def _run(cmd):
 # which no other instruction of those kernels uses (the warning about
 # clobbering a reserved register is silenced).
 # The backward kernels also take the compiler's ILP-first scheduling strategy
-# (measured 1.7% faster than the default; the forward kernels measured slower
-# with it).
+# (measured 0.5-1.2% faster than the default at 8K and 16K, slower only on
+# the smallest d = 64 shapes; the forward kernels measured slower with it).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-Wno-inline-asm"]
 EXTRA = {"fa_fwd_bf16.hip": _VGPR_FORM, "fa_fwd_fp8.hip": _VGPR_FORM,
          "fa_bwd.hip": _VGPR_FORM + ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
