@@ -131,3 +131,42 @@ def test_one_long_sequence():
     ref, _ = oracle.decode(si.as_float64(q, "bf16"), si.as_float64(k, "bf16"), si.as_float64(v, "bf16"))
     for ns, got in outs.items():
         print("long sequence, nsplit", ns, assert_close(got, ref, "bf16"))
+
+
+def test_concurrent_host_threads_on_their_own_streams():
+    """Four host threads, each with its own stream, decode shapes of growing size at the same time
+    (each stream's workspace is created and regrown under the library's lock while the others run);
+    every result equals the same call made alone."""
+    import threading
+    shapes = [(2, 3, 700, 128, 16), (1, 4, 5000, 64, 64), (3, 2, 20000, 128, 128), (2, 2, 333, 128, 5)]
+    cases = []
+    for i, (B, H, L, d, ns) in enumerate(shapes):
+        q, k, v = si.random_case(600 + i, B, H, 1, d, "bf16", nk=L)
+        cases.append((to_device(q[:, :, 0, :], "bf16"), to_device(k, "bf16"), to_device(v, "bf16"), ns))
+    alone = [fa.decode(qd, kd, vd, nsplit=ns) for qd, kd, vd, ns in cases]
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = []
+                for rep in range(3):
+                    for j in range(len(cases)):
+                        qd, kd, vd, ns = cases[(t + j) % len(cases)]
+                        outs.append(((t + j) % len(cases), fa.decode(qd, kd, vd, nsplit=ns)))
+            s.synchronize()
+            results[t] = outs
+        except Exception as e:  # reported below, with the thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    for t in range(4):
+        for j, o in results[t]:
+            assert torch.equal(o, alone[j]), (t, j)
