@@ -68,6 +68,8 @@ enum fa_status {
  * Arithmetic: bf16 MFMA products with fp32 accumulation; softmax in fp32; the
  * probabilities are rounded to bf16 (round to nearest even) for the P V
  * product; O is divided by the row sum in fp32 and rounded once to bf16.
+ * The dot products and the scaled logits are fp32 values: a row whose logits
+ * (scale * q.k, in base-2 units) leave the fp32 range gets non-finite outputs.
  * Uses no workspace and allocates nothing.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
