@@ -23,7 +23,10 @@
 //    recomputes S = Q K^T and dP = dO V^T (lane l holds key l % 32 and 16
 //    queries), forms P and dS in registers and accumulates dV += P^T dO and
 //    dK += dS^T Q, the P^T / dS^T operands coming straight from those
-//    registers and dO / Q through the transposing LDS read. The second wave
+//    registers and dO / Q through the transposing LDS read. The step is laid
+//    out as a chain in which each stretch of arithmetic sits under MFMAs that
+//    do not need it: S, then dP with P formed between its MFMAs, then dV with
+//    dS formed between them, then dK. The second wave
 //    of each pair adds its sums into the first's through LDS at the end;
 //  * bwd_dq: one workgroup per 256 queries (8 waves x 32 rows), laid out like
 //    the forward: S^T = K Q^T and dP^T = V dO^T with Q / dO in VGPRs, then
@@ -265,50 +268,64 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(const uint16_t* __rest
           for (int i = 0; i < 4; ++i) dp[4 * rb + i] = x[i];
         }
       }
-      // S = Q K^T and dP - D = dO V^T - D over the head dim
+      // S = Q K^T over the head dim; then dP - D = dO V^T - D with the
+      // probabilities P = exp2(S c2 - LSE2) formed between those MFMAs; then
+      // dV += P^T dO with dS = P (dP - D) formed between them; then dK += dS^T Q
       f32x16 sc = (f32x16){};
 #pragma unroll
-      for (int c = 0; c < T::NC; ++c) {
-        sc = mfma32x32x16(row_frag(lds, tQ, tl, par, c), row_frag(lds, tK, tl, hk, c), sc);
-        dp = mfma32x32x16(row_frag(lds, tdO, tl, par, c), row_frag(lds, tV, tl, hk, c), dp);
-      }
-      if ((qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31)) {
+      for (int c = 0; c < T::NC; ++c) sc = mfma32x32x16(row_frag(lds, tQ, tl, par, c), row_frag(lds, tK, tl, hk, c), sc);
+      const bool edge = (qb0 + 32 > N) || (CAUSAL && qb0 < kw0 + 31);
+      if (edge) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
-          if (!(q < N && (!CAUSAL || key <= q))) {
-            sc[r] = -INFINITY;  // P = 0
-            dp[r] = 0.f;        // dS = 0 * 0 = 0 whatever the row data holds
-          }
+          if (!(q < N && (!CAUSAL || key <= q))) sc[r] = -INFINITY;  // P = 0
         }
       }
-      // P = exp2(S c2 - LSE2) and dS = P (dP - D), packed as the bf16 A
-      // operands of the next MFMAs (k-slots: the lane's queries)
       const float* stats = (const float*)(lds + tQ + 2 * T::BYTES);  // [LSE2 x 64][-D x 64]
+      float pr[16];
       bf16x8 pb[2], sb[2];
+      constexpr int PPM = 8 / T::NC;  // probability pairs per dP MFMA
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f32x4 L = *(const f32x4*)(stats + 32 * par + 8 * rb + 4 * hf);
+      for (int c = 0; c < T::NC; ++c) {
+        dp = mfma32x32x16(row_frag(lds, tdO, tl, par, c), row_frag(lds, tV, tl, hk, c), dp);
 #pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const int r = 4 * rb + e;
-          const float p0 = fast_exp2(fmaf(sc[r], c2, -L[e]));
-          const float p1 = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
-          const bf16x2 pp = to_bf16x2(p0, p1), ss = to_bf16x2(p0 * dp[r], p1 * dp[r + 1]);
+        for (int j = 0; j < PPM; ++j) {
+          const int r = 2 * (PPM * c + j), rb = r >> 2, e = r & 3;
+          const f32x4 L = *(const f32x4*)(stats + 32 * par + 8 * rb + 4 * hf);
+          pr[r] = fast_exp2(fmaf(sc[r], c2, -L[e]));
+          pr[r + 1] = fast_exp2(fmaf(sc[r + 1], c2, -L[e + 1]));
+          const bf16x2 pp = to_bf16x2(pr[r], pr[r + 1]);
           pb[r >> 3][r & 7] = pp[0];
           pb[r >> 3][(r & 7) + 1] = pp[1];
-          sb[r >> 3][r & 7] = ss[0];
-          sb[r >> 3][(r & 7) + 1] = ss[1];
         }
       }
-      // dV += P^T dO and dK += dS^T Q, dO / Q through the transposing read
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb0 + 8 * (r >> 2) + 4 * hf + (r & 3), key = kw0 + lq;
+          if (!(q < N && (!CAUSAL || key <= q))) dp[r] = 0.f;  // dS = 0 * 0 = 0 whatever the row data holds
+        }
+      }
+      // dV += P^T dO (dO through the transposing read), dS between them
+      constexpr int SPM = 8 / (2 * T::NDB);  // dS pairs per dV MFMA
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
         for (int db = 0; db < T::NDB; ++db) {
           dv[db] = mfma32x32x16(pb[kc], tr_frag(lds, tdO, tl, par, kc, db), dv[db]);
-          dk[db] = mfma32x32x16(sb[kc], tr_frag(lds, tQ, tl, par, kc, db), dk[db]);
+#pragma unroll
+          for (int j = 0; j < SPM; ++j) {
+            const int r = 2 * (SPM * (kc * T::NDB + db) + j);
+            const bf16x2 ss = to_bf16x2(pr[r] * dp[r], pr[r + 1] * dp[r + 1]);
+            sb[r >> 3][r & 7] = ss[0];
+            sb[r >> 3][(r & 7) + 1] = ss[1];
+          }
         }
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int db = 0; db < T::NDB; ++db) dk[db] = mfma32x32x16(sb[kc], tr_frag(lds, tQ, tl, par, kc, db), dk[db]);
     }
     // end of tile t: tile t + 1 has landed for every wave and every wave is
     // done with tile t, whose slot then receives tile t + 2
