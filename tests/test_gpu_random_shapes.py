@@ -103,7 +103,11 @@ def test_fuzz_every_entry_point():
     rng = np.random.default_rng(seed)
     kinds = ["fwd"] * 5 + ["bwd"] * 2 + ["dec"] * 2 + ["paged"] * 2 + ["fp8"] * 2
     counts, fails, n, t0 = {}, [], 0, time.time()
+    t_report = t0
     while time.time() - t0 < budget:
+        if time.time() - t_report > 20:  # a progress line for long budgets
+            t_report = time.time()
+            print(f"fuzz seed {seed}: {n} cases, {len(fails)} failed, {t_report - t0:.0f} s", flush=True)
         kind = kinds[int(rng.integers(0, len(kinds)))]
         s = 10000 + n
         if kind == "fwd":
