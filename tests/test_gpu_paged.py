@@ -46,7 +46,10 @@ def test_ragged_lengths(d, page_size):
     """Seeded ragged lengths: 1, page-1, page, page+1 and Lmax keys, then uniform draws."""
     q, kp, vp, table, lens = paged_case(page_size + d, 7, 3, 1100, d, page_size)
     got = run_paged(q, kp, vp, table, lens, nsplit=16)
-    assert_close(got, oracle_paged(q, kp, vp, table, lens), "bf16")
+    ref = oracle_paged(q, kp, vp, table, lens)
+    assert_close(got, ref, "bf16")
+    for b in range(len(lens)):  # and each sequence alone: short rows would dominate the whole-tensor norm
+        assert_close(got[b], ref[b], "bf16", what=f"sequence {b} ({int(lens[b])} keys)")
 
 
 @pytest.mark.parametrize("nsplit", [1, 3, 64, 777, 5000])
@@ -138,3 +141,14 @@ def test_long_sequences_in_large_pages():
     q, kp, vp, table, lens = paged_case(81, 2, 1, Lmax, 128, 64, lens=[Lmax, 300001])
     got = run_paged(q, kp, vp, table, lens, 64)
     print("paged long sequences", assert_close(got, oracle_paged(q, kp, vp, table, lens), "bf16"))
+
+
+def test_largest_page_size():
+    """Pages of 65,536 keys (the largest page size accepted), five sequences of 1, 65,535, 65,536, 65,537 and
+    70,000 keys (one or two pages each, the rest of each page NaN)."""
+    Lmax, ps = 70000, 65536
+    q, kp, vp, table, lens = paged_case(91, 5, 1, Lmax, 128, ps, lens=[1, ps - 1, ps, ps + 1, Lmax])
+    got = run_paged(q, kp, vp, table, lens, nsplit=16)
+    ref = oracle_paged(q, kp, vp, table, lens)
+    for b in range(5):  # each sequence on its own: the one-key row would dominate a whole-tensor norm
+        print("largest pages, length", int(lens[b]), assert_close(got[b], ref[b], "bf16"))
