@@ -14,6 +14,16 @@ BF16_LSE_ABS = 1e-3
 F32_REL_L2 = 1e-5
 F32_MAX_ABS = 1e-4
 F32_LSE_ABS = 1e-5
+# Per output row (the last axis, d values): relative L2 of each row on its own. The whole-tensor bound above is
+# dominated by the rows of largest norm (in a causal pass the early rows, which see few keys), so an error
+# confined to the small late rows could hide under it. Bound: the output's rounding to bf16 moves each element
+# by at most 2^-8 of itself, and the probabilities' rounding moves a row by at most 2^-8 where one key dominates
+# it (spread over many keys the errors average out), so a row's relative error stays below 2^-7 ~ 7.8e-3;
+# measured worst rows are 4.7e-3 (forward, logit spread up to 2.5) and 2.0e-3 (decode). A row whose norm is
+# below ROW_FLOOR * sqrt(d) is held to that absolute level instead.
+BF16_ROW_REL = 1e-2
+F32_ROW_REL = 1e-4
+ROW_FLOOR = 1e-3
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -34,16 +44,30 @@ def metrics(out: np.ndarray, ref: np.ndarray):
     return rel, float(np.max(np.abs(diff))) if diff.size else 0.0
 
 
+def worst_row(out: np.ndarray, ref: np.ndarray):
+    """Largest per-row relative L2 (rows along the last axis) and its flat row index."""
+    d = out.shape[-1]
+    o2, r2 = out.reshape(-1, d), ref.reshape(-1, d)
+    if o2.shape[0] == 0:
+        return 0.0, -1
+    ratio = np.linalg.norm(o2 - r2, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), ROW_FLOOR * np.sqrt(d))
+    i = int(np.argmax(ratio))
+    return float(ratio[i]), i
+
+
 def assert_close(out, ref, dtype: str, what: str = "O"):
     rel, mx = metrics(out, ref)
+    row, at = worst_row(out, ref)
     if dtype == "bf16":
         assert np.isfinite(out).all(), f"{what}: non-finite values"
         assert rel <= BF16_REL_L2, f"{what}: relative L2 {rel:.3e} > {BF16_REL_L2}"
         assert mx <= BF16_MAX_ABS, f"{what}: max abs {mx:.3e} > {BF16_MAX_ABS}"
+        assert row <= BF16_ROW_REL, f"{what}: row {at} relative L2 {row:.3e} > {BF16_ROW_REL}"
     else:
         assert np.isfinite(out).all(), f"{what}: non-finite values"
         assert rel <= F32_REL_L2, f"{what}: relative L2 {rel:.3e} > {F32_REL_L2}"
         assert mx <= F32_MAX_ABS, f"{what}: max abs {mx:.3e} > {F32_MAX_ABS}"
+        assert row <= F32_ROW_REL, f"{what}: row {at} relative L2 {row:.3e} > {F32_ROW_REL}"
     return rel, mx
 
 
