@@ -106,6 +106,7 @@ class WholeTensorCheck:
         self.max_abs = 0.0
         self.lse_abs = 0.0
         self.worst_head = (0.0, None)
+        self.worst_row = (0.0, None)
         self.heads = 0
         self.finite = True
 
@@ -120,6 +121,9 @@ class WholeTensorCheck:
         head_rel = (e2 / r2) ** 0.5 if r2 > 0 else 0.0
         if head_rel >= self.worst_head[0]:
             self.worst_head = (head_rel, key)
+        row, at = worst_row(got, ref)
+        if row >= self.worst_row[0]:
+            self.worst_row = (row, (key, at))
         if got_lse is not None:
             gl = np.asarray(got_lse, np.float64)
             self.finite = self.finite and bool(np.isfinite(gl).all())
@@ -132,7 +136,8 @@ class WholeTensorCheck:
 
     def summary(self) -> dict:
         return {"heads": self.heads, "rel_l2": self.rel_l2, "max_abs": self.max_abs, "lse_max_abs": self.lse_abs,
-                "worst_head_rel_l2": self.worst_head[0], "worst_head": self.worst_head[1]}
+                "worst_head_rel_l2": self.worst_head[0], "worst_head": self.worst_head[1],
+                "worst_row_rel_l2": self.worst_row[0], "worst_row": self.worst_row[1]}
 
     def assert_bounds(self, with_lse: bool = True):
         rel_b, abs_b, lse_b = ((BF16_REL_L2, BF16_MAX_ABS, BF16_LSE_ABS) if self.dtype == "bf16"
@@ -141,6 +146,8 @@ class WholeTensorCheck:
         assert self.finite, f"non-finite outputs: {s}"
         assert self.rel_l2 <= rel_b, f"whole-tensor relative L2 {self.rel_l2:.3e} > {rel_b}: {s}"
         assert self.max_abs <= abs_b, f"max abs {self.max_abs:.3e} > {abs_b}: {s}"
+        row_b = BF16_ROW_REL if self.dtype == "bf16" else F32_ROW_REL
+        assert self.worst_row[0] <= row_b, f"row relative L2 {self.worst_row[0]:.3e} > {row_b}: {s}"
         if with_lse:
             assert self.lse_abs <= lse_b, f"LSE max abs {self.lse_abs:.3e} > {lse_b}: {s}"
         return s
